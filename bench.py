@@ -1,0 +1,183 @@
+"""Benchmark of the MI355X tree-verify MLA-absorb attention.
+
+One step = one kdtree_verify_attn call over the whole batch (one layer's verify
+attention for every request) of the batch-64 ragged workload: H=64, q_len 33,
+prefixes uniform in [1024, 8192] stored contiguously, half wide (top-8) / half deep
+(top-2) best-first trees, bf16 inputs, fp32 output.  Inputs are synthetic, seeded, and
+resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0):
+  value      = algorithmic TFLOP/s (2*(576+512) flops per visible (row, key) pair)
+  roofline   = the attention kernel vs the bf16 dense MFMA peak (2.5 PFLOP/s), from
+               HIP events on the launch stream over the timed region
+  cpu_baseline = the float64 oracle on a bounded sample of the same workload
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify_attn TFLOP/s and tree-verify steps/s (H=64, q_len 33/65); % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="1..5 (default: batch-64 ragged)")
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one 256 MiB device copy (reference for HBM counters)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, seconds):
+    """Time the float64 oracle request by request until `seconds` have elapsed."""
+    import numpy as np
+    from oracle import verify_attn_f64 as O
+    from tree_verify_mla_attn_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    qo, ko = inp.q_offsets(), inp.kv_offsets()
+    flops = 0
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(inp.batch):
+        t, p = int(inp.q_len[b]), int(inp.prefix_len[b])
+        O.verify_attn(inp.q_lat[qo[b]:qo[b] + t], inp.q_rope[qo[b]:qo[b] + t],
+                      inp.kv_lat[ko[b]:ko[b] + p + t], inp.k_rope[ko[b]:ko[b] + p + t], [p],
+                      inp.parents_of(b), [t], inp.scale)
+        dep = synth.tree_depths(inp.parents_of(b)).astype(np.int64)
+        flops += int((p + dep + 1).sum()) * inp.num_heads * 2 * (576 + 512)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle on the first {done} of {inp.batch} requests "
+                      f"({flops:.3e} algorithmic FLOPs in {dt:.2f} s, BLAS threads={threads}, "
+                      f"host cpus={os.cpu_count()})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernel works "
+              "on one GPU's share and there is no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from tree_verify_mla_attn_amd import binding as B
+    from tree_verify_mla_attn_amd import synth
+
+    B.load_library()
+    dev = torch.device("cuda:0")
+    inp = synth.config_inputs(args.workload)
+    splits = args.num_splits or inp.num_splits
+    d = synth.device_tensors(inp, dev)
+    flops = inp.algorithmic_flops()
+    alg_bytes = inp.algorithmic_bytes()
+    call = B.VerifyAttn()
+    out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)
+    ws = None
+    if splits > 1:
+        ws = torch.empty(B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.num_heads, splits),
+                         dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    argv = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
+            d["q_len"], inp.scale)
+
+    def step():
+        call(*argv, out_lat=out, out_lse=lse, num_splits=splits, max_q_len=inp.max_q_len,
+             workspace=ws, status=status)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    st = int(status.item())
+    if st:
+        raise RuntimeError(f"device status {B.decode_status(st)}")
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = wall * 1e3 / args.steps
+    ev_ms = sum(per_launch_ms) / len(per_launch_ms)
+
+    dtype = inp.dtype
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == inp.name and tj.get("num_splits") == splits:
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "steps_per_s": round(1e3 / ms, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) MLA tensors, best-first draft trees)",
+        "config": {"workload": inp.name, "batch": inp.batch, "heads": inp.num_heads,
+                   "q_len": int(inp.max_q_len), "total_q": inp.total_q, "total_kv": inp.total_kv,
+                   "num_splits": splits, "d_latent": 512, "d_rope": 64,
+                   "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
+        "hbm": {"achieved_GBs": round(alg_bytes / (ev_ms * 1e-3) / 1e9, 1),
+                "peak_GBs": HBM_PEAK_GBS,
+                "frac": round(alg_bytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "event_ms_per_launch": round(ev_ms, 5),
+    }
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(f"calibration copy: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written",
+              file=sys.stderr, flush=True)
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed: every call here fails validation before
+anything is enqueued, or is a pure size query)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tree_verify_mla_attn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdtree_verify.h")
+FAKE = 0x1000  # never dereferenced: these calls fail host validation first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdtree_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    names = _declared_functions()
+    assert names == ["kdtree_max_qlen", "kdtree_verify_attn", "kdtree_verify_attn_workspace_bytes"]
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True,
+                         text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), f"{n} not a defined text symbol"
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert re.search(r"#define KDTREE_MAX_QLEN 65\b", text)
+    assert B.kdtree_max_qlen() == 65 == B.KDTREE_MAX_QLEN
+    for code in B.ERRORS:
+        if code:
+            assert re.search(rf"\(({code})\)", text), f"error code {code} missing from header"
+
+
+def test_workspace_bytes():
+    assert B.kdtree_verify_attn_workspace_bytes(100, 64, 1) == 0
+    n = B.kdtree_verify_attn_workspace_bytes(260, 64, 16)
+    rows = 260 * 64
+    o_bytes = -(-16 * rows * 512 * 4 // 256) * 256
+    assert n == -(-(o_bytes + 16 * rows * 4) // 256) * 256
+    assert n % 256 == 0
+    assert B.kdtree_verify_attn_workspace_bytes(0, 64, 2) == 0
+    assert B.kdtree_verify_attn_workspace_bytes(10, 64, 0) == 0
+    assert B.kdtree_verify_attn_workspace_bytes(10, 64, 257) == 0
+
+
+def _call(**kw):
+    args = dict(q_lat=FAKE, q_rope=FAKE, kv_lat=FAKE, k_rope=FAKE, prefix_len=FAKE,
+                tree_parent=FAKE, q_len=FAKE, scale=0.07, out_lat=FAKE, out_lse=FAKE, stream=0,
+                batch=2, num_heads=64, max_q_len=33, total_q=66, total_kv=2000, dtype=1,
+                num_splits=1, workspace=0, workspace_bytes=0, status=0)
+    args.update(kw)
+    return B.kdtree_verify_attn(**args)
+
+
+@pytest.mark.parametrize("field", ["q_lat", "q_rope", "kv_lat", "k_rope", "prefix_len",
+                                   "tree_parent", "q_len", "out_lat", "out_lse"])
+def test_null_pointer_rejected(field):
+    assert _call(**{field: 0}) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -2), (dict(num_heads=0), -2), (dict(total_q=1), -2),
+    (dict(total_kv=10), -2), (dict(max_q_len=0), -3), (dict(max_q_len=66), -3),
+    (dict(dtype=2), -4), (dict(dtype=-1), -4), (dict(num_splits=0), -5),
+    (dict(num_splits=300), -5), (dict(num_splits=4), -5),
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), -5),
+    (dict(scale=float("nan")), -6), (dict(scale=float("inf")), -6),
+])
+def test_bad_arguments_rejected(kw, code):
+    assert _call(**kw) == code
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "tree_verify_mla_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
+                assert "oracle/" not in text, f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setenv("KDTREE_LIB", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError):
+        B.load_library()
+    monkeypatch.setattr(B, "_lib", None)
+
+
+def test_choose_num_splits():
+    # few row tiles + long prefixes -> more splits; many tiles -> none
+    assert B.choose_num_splits(1, 64, 33, 2081) >= 2
+    assert B.choose_num_splits(64, 64, 33, 5000) == 1
+    assert B.choose_num_splits(4, 64, 65, 32833) >= 2

@@ -1,0 +1,238 @@
+"""GPU parity of the HIP tree-verify attention against the float64 oracle.
+
+Bars: fp32 inputs -> max |gpu - oracle| <= 1e-5 on out_lat and out_lse; bf16 inputs ->
+|gpu - oracle| <= 1e-3 + 2e-3 |oracle| elementwise, oracle fed the same bf16 values.
+Small cases compare every element; the large workloads (batch 8 / 64 / 4 at H=64) run in
+the launch configuration the benchmark times and compare sampled rows that the oracle
+computes one by one, plus whole-output properties.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import verify_attn_inputs, verify_attn_rows
+from tree_verify_mla_attn_amd import binding as B
+from tree_verify_mla_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+FP32_ATOL = 1e-5
+BF16_ATOL, BF16_RTOL = 1e-3, 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+    return torch.device("cuda:0")
+
+
+def run(inp, dev, num_splits=1, max_q_len=None):
+    d = synth.device_tensors(inp, dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out, lse = B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+                             d["tree_parent"], d["q_len"], inp.scale, num_splits=num_splits,
+                             max_q_len=max_q_len or inp.max_q_len, status=status)
+    torch.cuda.synchronize(dev)
+    return out, lse, int(status.item())
+
+
+def check(name, inp, g_out, g_lse, r_out, r_lse):
+    g_out = np.asarray(g_out, np.float64)
+    g_lse = np.asarray(g_lse, np.float64)
+    e_out = np.abs(g_out - r_out)
+    e_lse = np.abs(g_lse - r_lse)
+    print(f"[{name}] max|d out|={e_out.max():.3e} max|d lse|={e_lse.max():.3e}", flush=True)
+    assert np.isfinite(g_out).all() and np.isfinite(g_lse).all()
+    if inp.dtype == "fp32":
+        assert e_out.max() <= FP32_ATOL, name
+        assert e_lse.max() <= FP32_ATOL, name
+    else:
+        bad = e_out > BF16_ATOL + BF16_RTOL * np.abs(r_out)
+        assert not bad.any(), f"{name}: {int(bad.sum())} out_lat elements outside tolerance"
+        assert not (e_lse > BF16_ATOL + BF16_RTOL * np.abs(r_lse)).any(), name
+
+
+def full_check(name, inp, dev, num_splits=1):
+    print(f"case {name} splits={num_splits}", flush=True)
+    out, lse, st = run(inp, dev, num_splits)
+    assert st == 0, B.decode_status(st)
+    r_out, r_lse = verify_attn_inputs(inp)
+    check(name, inp, out.double().cpu().numpy(), lse.double().cpu().numpy(), r_out, r_lse)
+    return out, lse
+
+
+# ------------------------------------------------------------------ small / edge cases
+def _mk(seed, parents, prefix, heads, dtype, scale=None):
+    rng = np.random.default_rng(seed)
+    return synth.make_inputs(rng, num_heads=heads, prefix_lens=prefix, parents=parents,
+                             dtype=dtype, scale=scale)
+
+
+EDGE = {
+    "chain9_p37_h64": lambda dt: _mk(1, [synth.chain_tree(9)], [37], 64, dt),
+    "star17_p0_h16": lambda dt: _mk(2, [synth.star_tree(17)], [0], 16, dt),
+    "deep15_p100_h8": lambda dt: _mk(3, [synth.chain_tree(16)], [100], 8, dt),
+    "root_only_p5_h64": lambda dt: _mk(4, [np.array([-1], np.int32)], [5], 64, dt),
+    "qlen65_p300_h64": lambda dt: _mk(5, [synth.random_tree(np.random.default_rng(9), 65)], [300],
+                                      64, dt),
+    "ragged_batch5_h64": lambda dt: _mk(
+        6, [synth.random_tree(np.random.default_rng(10 + i), n) for i, n in
+            enumerate((1, 9, 33, 65, 17))], [0, 31, 64, 257, 1000], 64, dt),
+    "tile_edges_h16": lambda dt: _mk(
+        7, [synth.random_tree(np.random.default_rng(20 + i), 33) for i in range(4)],
+        [31, 32, 33, 64], 16, dt),
+    "zero_scale": lambda dt: _mk(8, [synth.random_tree(np.random.default_rng(30), 12)], [40], 64,
+                                 dt, scale=0.0),
+    "negative_scale": lambda dt: _mk(9, [synth.random_tree(np.random.default_rng(31), 12)], [40],
+                                     64, dt, scale=-0.08),
+}
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(dev, case, dtype):
+    full_check(f"{case}/{dtype}", EDGE[case](dtype), dev)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("splits", [2, 3, 16])
+def test_split_kv(dev, splits, dtype):
+    inp = EDGE["ragged_batch5_h64"](dtype)
+    full_check(f"ragged_batch5/{dtype}", inp, dev, num_splits=splits)
+    inp = EDGE["deep15_p100_h8"](dtype)
+    full_check(f"deep15/{dtype}", inp, dev, num_splits=splits)
+
+
+def test_bf16_best_first_trees_several_tiles(dev):
+    rng = np.random.default_rng(40)
+    parents = [synth.best_first_tree(synth.logprob_table(rng, k), 32)[0] for k in (8, 2, 4)]
+    inp = synth.make_inputs(rng, num_heads=64, prefix_lens=[513, 200, 1030], parents=parents,
+                            dtype="bf16")
+    full_check("bestfirst3", inp, dev)
+    full_check("bestfirst3", inp, dev, num_splits=4)
+
+
+# ------------------------------------------------------------------ workloads
+def test_workload1_full(dev):
+    full_check("workload1", synth.config_inputs(1), dev)
+
+
+def test_workload2_full(dev):
+    inp = synth.config_inputs(2)
+    full_check("workload2", inp, dev)
+    full_check("workload2", inp, dev, num_splits=8)
+
+
+def _sample_rows(inp, rng, per_request_nodes=3, heads=(0, 63)):
+    picks = []
+    for b in range(inp.batch):
+        par = inp.parents_of(b)
+        dep = synth.tree_depths(par)
+        nodes = {0, len(par) - 1, int(np.argmax(dep))}
+        nodes |= set(int(x) for x in rng.integers(0, len(par), per_request_nodes))
+        hs = set(heads) | set(int(x) for x in rng.integers(0, inp.num_heads, 2))
+        picks.append((b, sorted(nodes), sorted(hs)))
+    return picks
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_large_workloads_sampled(dev, cfg):
+    inp = synth.config_inputs(cfg)
+    splits = inp.num_splits
+    print(f"case workload{cfg} splits={splits}", flush=True)
+    out, lse, st = run(inp, dev, splits)
+    assert st == 0, B.decode_status(st)
+    out_np = out.cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    assert np.isfinite(out_np).all() and np.isfinite(lse_np).all()
+    assert np.abs(out_np).max() <= np.abs(inp.kv_lat).max() + 1e-3  # convex combination
+    qo = inp.q_offsets()
+    rng = np.random.default_rng(cfg)
+    picks = _sample_rows(inp, rng, per_request_nodes=2 if cfg == 4 else 4)
+    g_o, g_l, r_o, r_l = [], [], [], []
+    for b, nodes, hs in picks:
+        ro, rl = verify_attn_rows(inp, b, nodes, hs)
+        rows = qo[b] + np.asarray(nodes)
+        g_o.append(out_np[rows][:, hs])
+        g_l.append(lse_np[rows][:, hs])
+        r_o.append(ro)
+        r_l.append(rl)
+    check(f"workload{cfg} sampled", inp, np.concatenate([x.reshape(-1, 512) for x in g_o]),
+          np.concatenate([x.ravel() for x in g_l]),
+          np.concatenate([x.reshape(-1, 512) for x in r_o]), np.concatenate([x.ravel() for x in r_l]))
+
+
+# ------------------------------------------------------------------ robustness
+def test_deterministic_and_guard_bands(dev):
+    inp = EDGE["ragged_batch5_h64"]("bf16")
+    d = synth.device_tensors(inp, dev)
+    tq, h = inp.total_q, inp.num_heads
+    results = []
+    for splits in (1, 4, 1):
+        big_o = torch.full((tq + 2, h, 512), 7.25, dtype=torch.float32, device=dev)
+        big_l = torch.full((tq + 2, h), 7.25, dtype=torch.float32, device=dev)
+        out, lse = big_o[1:tq + 1], big_l[1:tq + 1]
+        B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+                      d["tree_parent"], d["q_len"], inp.scale, out_lat=out, out_lse=lse,
+                      num_splits=splits, max_q_len=inp.max_q_len)
+        torch.cuda.synchronize(dev)
+        assert (big_o[0] == 7.25).all() and (big_o[-1] == 7.25).all()
+        assert (big_l[0] == 7.25).all() and (big_l[-1] == 7.25).all()
+        results.append((out.clone(), lse.clone()))
+    assert torch.equal(results[0][0], results[2][0]) and torch.equal(results[0][1], results[2][1])
+
+
+def test_malformed_inputs_set_status(dev):
+    base = EDGE["ragged_batch5_h64"]("bf16")
+    cases = []
+    bad_parent = base.tree_parent.copy()
+    bad_parent[3] = 7                               # request 1 node 2: parent must be < 2
+    cases.append(("bad_parent", dict(tree_parent=bad_parent), 4))
+    bad_q = base.q_len.copy()
+    bad_q[2] = 0
+    cases.append(("bad_qlen", dict(q_len=bad_q), 1))
+    bad_p = base.prefix_len.copy()
+    bad_p[1] = -3
+    cases.append(("bad_prefix", dict(prefix_len=bad_p), 2))
+    big_p = base.prefix_len.copy()
+    big_p[4] = 10 ** 6
+    cases.append(("overflow", dict(prefix_len=big_p), 8))
+    for name, change, bit in cases:
+        inp = synth.VerifyInputs(**{**base.__dict__, **change})
+        d = synth.device_tensors(inp, dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+                      d["tree_parent"], d["q_len"], inp.scale, num_splits=1,
+                      max_q_len=65, status=status)
+        torch.cuda.synchronize(dev)
+        st = int(status.item())
+        print(f"{name}: status {st} {B.decode_status(st)}", flush=True)
+        assert st & bit, name
+
+
+def test_hip_graph_capture_replays(dev):
+    inp = EDGE["qlen65_p300_h64"]("bf16")
+    d = synth.device_tensors(inp, dev)
+    call = B.VerifyAttn()
+    out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.num_heads, 4),
+                     dtype=torch.uint8, device=dev)
+    args = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
+            d["q_len"], inp.scale)
+    call(*args, out_lat=out, out_lse=lse, num_splits=4, max_q_len=65, workspace=ws)
+    torch.cuda.synchronize(dev)
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(*args, out_lat=out, out_lse=lse, num_splits=4, max_q_len=65, workspace=ws)
+    for i in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"

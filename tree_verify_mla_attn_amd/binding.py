@@ -1,0 +1,168 @@
+"""Thin ctypes binding of ``libkdtree_verify.so`` (C ABI in include/kdtree_verify.h).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels.  The
+bridge shape -- raw device pointers from torch tensors, the caller's current stream,
+the library found through ``$KDTREE_LIB`` or next to the package -- follows "The
+Capstone Commit: Validating a Native CUDA DDTree Inference Engine", section "The
+Message Itself" (commit body: ctypes bindings accepting device tensors and the current
+stream, loaded via an environment variable or the build directory).
+
+There is no fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(HERE, "libkdtree_verify.so")
+
+KDTREE_MAX_QLEN = 65
+KDTREE_DTYPE_FP32 = 0
+KDTREE_DTYPE_BF16 = 1
+ERRORS = {0: "OK", -1: "null pointer", -2: "bad shape", -3: "bad max_q_len", -4: "bad dtype",
+          -5: "bad num_splits / workspace", -6: "non-finite scale", -7: "HIP launch failure"}
+STATUS_BITS = {1: "bad q_len", 2: "bad prefix_len", 4: "bad tree_parent", 8: "offset overflow",
+               16: "non-finite output"}
+D_LATENT = 512
+D_ROPE = 64
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.environ.get("KDTREE_LIB") or DEFAULT_LIB
+
+
+def load_library():
+    """Load the HIP library (once).  Raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not found at {path}; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kdtree_max_qlen.restype = i32
+    lib.kdtree_max_qlen.argtypes = []
+    lib.kdtree_verify_attn_workspace_bytes.restype = sz
+    lib.kdtree_verify_attn_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.kdtree_verify_attn.restype = i32
+    lib.kdtree_verify_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                       i32, i32, i32, i64, i64, i32, i32, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- C entry points
+def kdtree_max_qlen() -> int:
+    return int(load_library().kdtree_max_qlen())
+
+
+def kdtree_verify_attn_workspace_bytes(total_q: int, num_heads: int, num_splits: int) -> int:
+    return int(load_library().kdtree_verify_attn_workspace_bytes(total_q, num_heads, num_splits))
+
+
+def kdtree_verify_attn(q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
+                       out_lat, out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv,
+                       dtype, num_splits, workspace, workspace_bytes, status) -> int:
+    """Raw call: every pointer argument is an integer device address (0 = NULL)."""
+    return int(load_library().kdtree_verify_attn(
+        q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, ctypes.c_float(scale),
+        out_lat, out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv, dtype,
+        num_splits, workspace, workspace_bytes, status))
+
+
+# ---------------------------------------------------------------- torch convenience
+def choose_num_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
+                      n_cu: int = 256, rows_per_block: int = 128, min_chunk: int = 512) -> int:
+    """Host-side split-KV heuristic for callers that know their prefix lengths: enough
+    workgroups to cover the chip about twice, chunks of at least ``min_chunk`` keys."""
+    blocks = batch * math.ceil(max_q_len * num_heads / rows_per_block)
+    s = 1
+    while s < 256 and blocks * s < 2 * n_cu and mean_kv / (2 * s) >= min_chunk:
+        s *= 2
+    return s
+
+
+class VerifyAttn:
+    """Reusable call object: checks and caches shapes, allocates outputs / workspace with
+    torch on the inputs' device, launches on the current stream."""
+
+    def __init__(self):
+        load_library()
+
+    @staticmethod
+    def _check(t, name, dtype, shape_tail, torch):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if tuple(t.shape[1:]) != tuple(shape_tail):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [*, {shape_tail}]")
+
+    def __call__(self, q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
+                 out_lat=None, out_lse=None, num_splits: int = 1,
+                 max_q_len: int = KDTREE_MAX_QLEN, workspace=None, status=None):
+        import torch
+        dtype = q_lat.dtype
+        if dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("inputs must be float32 or bfloat16")
+        if q_lat.dim() != 3:
+            raise ValueError("q_lat must be [total_q, H, 512]")
+        total_q, h = int(q_lat.shape[0]), int(q_lat.shape[1])
+        self._check(q_lat, "q_lat", dtype, (h, D_LATENT), torch)
+        self._check(q_rope, "q_rope", dtype, (h, D_ROPE), torch)
+        self._check(kv_lat, "kv_lat", dtype, (D_LATENT,), torch)
+        self._check(k_rope, "k_rope", dtype, (D_ROPE,), torch)
+        if int(q_rope.shape[0]) != total_q or int(k_rope.shape[0]) != int(kv_lat.shape[0]):
+            raise ValueError("row counts of q_lat/q_rope or kv_lat/k_rope differ")
+        batch = int(q_len.shape[0])
+        for t, n, rows in ((prefix_len, "prefix_len", batch), (q_len, "q_len", batch),
+                           (tree_parent, "tree_parent", total_q)):
+            if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1 \
+                    or int(t.shape[0]) != rows:
+                raise ValueError(f"{n} must be a contiguous int32 GPU vector of length {rows}")
+        dev = q_lat.device
+        if out_lat is None:
+            out_lat = torch.empty((total_q, h, D_LATENT), dtype=torch.float32, device=dev)
+        if out_lse is None:
+            out_lse = torch.empty((total_q, h), dtype=torch.float32, device=dev)
+        if out_lat.dtype != torch.float32 or out_lse.dtype != torch.float32 \
+                or tuple(out_lat.shape) != (total_q, h, D_LATENT) or tuple(out_lse.shape) != (total_q, h) \
+                or not out_lat.is_contiguous() or not out_lse.is_contiguous():
+            raise ValueError("out_lat / out_lse must be contiguous float32 [total_q, H, 512] / [total_q, H]")
+        need = kdtree_verify_attn_workspace_bytes(total_q, h, num_splits)
+        if num_splits > 1:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() if (workspace is not None and num_splits > 1) else 0
+        ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = kdtree_verify_attn(
+            q_lat.data_ptr(), q_rope.data_ptr(), kv_lat.data_ptr(), k_rope.data_ptr(),
+            prefix_len.data_ptr(), tree_parent.data_ptr(), q_len.data_ptr(), float(scale),
+            out_lat.data_ptr(), out_lse.data_ptr(), stream, batch, h, int(max_q_len), total_q,
+            int(kv_lat.shape[0]),
+            KDTREE_DTYPE_BF16 if dtype == torch.bfloat16 else KDTREE_DTYPE_FP32,
+            int(num_splits), ws_ptr, ws_bytes, status.data_ptr() if status is not None else 0)
+        if rc != 0:
+            raise RuntimeError(f"kdtree_verify_attn failed: {rc} ({ERRORS.get(rc, '?')})")
+        return out_lat, out_lse
+
+
+def verify_attn(*args, **kwargs):
+    """verify_attn(q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
+    out_lat=None, out_lse=None, num_splits=1, max_q_len=65, workspace=None, status=None)
+    -> (out_lat [total_q, H, 512] fp32, out_lse [total_q, H] fp32)."""
+    return VerifyAttn()(*args, **kwargs)
+
+
+def decode_status(value: int):
+    return [name for bit, name in STATUS_BITS.items() if value & bit]

@@ -1,0 +1,319 @@
+// Tree-verify MLA-absorb attention, fp32 inputs, gfx950.
+//
+// Same operation as the bf16 kernel ("The Milestone Commit: Cementing Phase 1 ...",
+// section "The Context", item 2), computed with fp32 MFMA (v_mfma_f32_16x16x4_f32) so
+// that products and sums stay in fp32.  One workgroup = 4 waves = 64 query rows; each
+// wave owns 16 rows with its Q fragment (16 x 576 fp32) in VGPRs.  Per 16-key tile:
+//   S^T = K Q^T  (16 keys x 16 rows per wave; each lane holds one query row),
+//   online softmax in the log2 domain with a lazy rescale,
+//   O^T += V^T P^T with V read straight from the fp32 tile (V = latent part of K).
+// The tile is staged through a padded, double-buffered LDS layout; the next tile's
+// global loads are in flight in VGPRs while the current tile is processed.
+#include "common.h"
+
+namespace kdt {
+namespace {
+
+constexpr int BM = 64;
+constexpr int BN = 16;
+constexpr int NTHR = 256;
+constexpr int KSTRIDE = DK + 4;  // floats per LDS key row (pad: conflict-free reads)
+constexpr float RESCALE_THRESHOLD = 8.0f;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__shared__ __attribute__((aligned(16))) float sK0[BN * KSTRIDE];
+__shared__ __attribute__((aligned(16))) float sK1[BN * KSTRIDE];
+__shared__ int32_t sParent32[MAX_QLEN];
+__shared__ int64_t sRed32[8];
+__shared__ int32_t sFlag32;
+
+template <int STAGE> __device__ __forceinline__ float* ktile() { return STAGE ? sK1 : sK0; }
+
+// Each thread moves 9 of the tile's 16 x 144 float4 chunks (latent chunks 0..127, rope
+// chunks 128..143 of every key).
+__device__ __forceinline__ void load_tile(float4 (&r)[9], const float* kv_lat, const float* k_rope,
+                                          int64_t kv_row0, int key0, int key_last, int tid) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int item = tid + NTHR * i;
+    const int key = item / 144, c = item % 144;
+    const int64_t k = kv_row0 + min(key0 + key, key_last);
+    r[i] = c < 128 ? *(const float4*)(kv_lat + k * DL + c * 4)
+                   : *(const float4*)(k_rope + k * DR + (c - 128) * 4);
+  }
+}
+
+template <int STAGE>
+__device__ __forceinline__ void store_tile(const float4 (&r)[9], int tid) {
+  float* kt = ktile<STAGE>();
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int item = tid + NTHR * i;
+    const int key = item / 144, c = item % 144;
+    *(float4*)(kt + key * KSTRIDE + c * 4) = r[i];
+  }
+}
+
+template <int STAGE>
+__device__ __forceinline__ f32x4 qk_tile(const float4 (&qf)[36], int lane) {
+  const float* kt = ktile<STAGE>();
+  const int key = lane & 15, g = lane >> 4;
+  // Four independent accumulation chains (one per float of the 16-byte operand), summed
+  // pairwise at the end: each chain adds 144 products, which keeps the fp32 rounding of
+  // the 576-term score well inside the 1e-5 output bound.
+  f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};
+#pragma unroll
+  for (int kb = 0; kb < 36; ++kb) {
+    const float4 a = *(const float4*)(kt + key * KSTRIDE + 16 * kb + 4 * g);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, qf[kb].x, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, qf[kb].y, s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, qf[kb].z, s2, 0, 0, 0);
+    s3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, qf[kb].w, s3, 0, 0, 0);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+template <int STAGE>
+__device__ __forceinline__ void pv_tile(f32x4 (&o)[32], const f32x4& pr, int lane) {
+  const float* kt = ktile<STAGE>();
+  const int fl = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int fb = 0; fb < 32; ++fb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = kt[(4 * g + r) * KSTRIDE + fb * 16 + fl];
+      o[fb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, pr[r], o[fb], 0, 0, 0);
+    }
+  }
+}
+
+struct RowState32 {
+  float m, l;
+};
+
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ void softmax_tile(f32x4& s, f32x4 (&o)[32], RowState32& st, float c,
+                                             bool masked, int tile_key0, int key_end, int prefix,
+                                             int node, uint64_t anc, int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    bool vis = true;
+    if (masked) {
+      const int k = tile_key0 + 4 * g + r;
+      vis = k < key_end;
+      if (k >= prefix) {
+        const int j = k - prefix;
+        vis = vis && (j == node || (j < 64 && ((anc >> j) & 1ull)));
+      }
+    }
+    s[r] = vis ? s[r] * c : -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  mx = row_max4(mx);
+  const bool need = mx > st.m + RESCALE_THRESHOLD;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float mnew = need ? mx : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.0f;
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int fb = 0; fb < 32; ++fb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[fb][r] *= alpha;
+  }
+  const float mref = st.m == -INFINITY ? 0.0f : st.m;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] = __builtin_amdgcn_exp2f(s[r] - mref);
+    st.l += s[r];
+  }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(1, 1)))
+void verify_attn_f32_kernel(VerifyParams p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+
+  int bid = blockIdx.x;
+  const int mt = bid % p.m_tiles;
+  bid /= p.m_tiles;
+  const int split = bid % p.num_splits;
+  const int b = bid / p.num_splits;
+
+  int64_t qoff = 0, kvoff = 0;
+  int bad = 0;
+  for (int i = tid; i < b; i += NTHR) {
+    const int t = p.q_len[i], pl = p.prefix_len[i];
+    bad |= (t < 1 || t > p.max_q_len) ? ST_BAD_QLEN : 0;
+    bad |= pl < 0 ? ST_BAD_PREFIX : 0;
+    qoff += t;
+    kvoff += (int64_t)pl + t;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    qoff += __shfl_xor(qoff, off);
+    kvoff += __shfl_xor(kvoff, off);
+    bad |= __shfl_xor(bad, off);
+  }
+  if (tid == 0) sFlag32 = 0;
+  __syncthreads();
+  if (lane == 0) {
+    sRed32[wave] = qoff;
+    sRed32[4 + wave] = kvoff;
+    if (bad) atomicOr(&sFlag32, bad);
+  }
+  __syncthreads();
+  qoff = sRed32[0] + sRed32[1] + sRed32[2] + sRed32[3];
+  kvoff = sRed32[4] + sRed32[5] + sRed32[6] + sRed32[7];
+  const int T = p.q_len[b];
+  const int P = p.prefix_len[b];
+  int flag = sFlag32;
+  if (T < 1 || T > p.max_q_len) flag |= ST_BAD_QLEN;
+  if (P < 0) flag |= ST_BAD_PREFIX;
+  if (!flag && (qoff + T > p.total_q || kvoff + P + T > p.total_kv || P > MAX_REQUEST_KEYS - T))
+    flag |= ST_OVERFLOW;
+  if (flag) {
+    if (tid == 0 && p.status) atomicOr(p.status, flag);
+    return;
+  }
+  const int H = p.num_heads;
+  const int rows = T * H;
+  const int m0 = mt * BM;
+  if (m0 >= rows) return;
+
+  __syncthreads();
+  if (tid == 0) sFlag32 = 0;
+  __syncthreads();
+  if (tid < T) {
+    const int pa = p.tree_parent[qoff + tid];
+    const bool ok = tid == 0 ? pa == -1 : (pa >= 0 && pa < tid);
+    sParent32[tid] = ok ? pa : -1;
+    if (!ok) atomicOr(&sFlag32, ST_BAD_PARENT);
+  }
+  __syncthreads();
+  if (sFlag32) {
+    if (tid == 0 && p.status) atomicOr(p.status, sFlag32);
+    return;
+  }
+
+  const int row = m0 + wave * 16 + (lane & 15);
+  const bool row_ok = row < rows;
+  const int crow = row_ok ? row : rows - 1;
+  const int node = crow / H;
+  uint64_t anc = 0;
+  for (int x = node, hops = 0; x >= 0 && hops <= MAX_QLEN; ++hops) {
+    if (x < 64) anc |= 1ull << x;
+    x = sParent32[x];
+  }
+
+  const int S = p.num_splits;
+  int k_begin, k_end;
+  {
+    const int chunk = (P + S - 1) / S;
+    k_begin = min(P, split * chunk);
+    k_end = (split == S - 1) ? P + T : min(P, (split + 1) * chunk);
+  }
+  const int64_t grow = qoff * H + crow;
+  if (k_end <= k_begin) {
+    if (row_ok) {
+      float* po = p.part_o + ((int64_t)split * p.total_q * H + grow) * DL;
+      for (int f = g * 4; f < DL; f += 16) *(float4*)(po + f) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (g == 0) p.part_lse[(int64_t)split * p.total_q * H + grow] = -INFINITY;
+    }
+    return;
+  }
+
+  float4 qf[36];
+  {
+    const float* ql = (const float*)p.q_lat + grow * DL;
+    const float* qr = (const float*)p.q_rope + grow * DR;
+#pragma unroll
+    for (int kb = 0; kb < 36; ++kb) {
+      const int f = 16 * kb + 4 * g;
+      qf[kb] = kb < 32 ? *(const float4*)(ql + f) : *(const float4*)(qr + f - DL);
+    }
+  }
+
+  const float* kv_lat = (const float*)p.kv_lat;
+  const float* k_rope = (const float*)p.k_rope;
+  const int key_last = k_end - 1;
+  const int n_tiles = (k_end - k_begin + BN - 1) / BN;
+  const int mask_from = min(P, k_end);
+  const float c = p.scale_log2;
+
+  f32x4 o[32];
+#pragma unroll
+  for (int fb = 0; fb < 32; ++fb) o[fb] = f32x4{};
+  RowState32 st{-INFINITY, 0.0f};
+
+  float4 pre[9];
+  load_tile(pre, kv_lat, k_rope, kvoff, k_begin, key_last, tid);
+  store_tile<0>(pre, tid);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; j += 2) {
+    {
+      const int key0 = k_begin + j * BN;
+      if (j + 1 < n_tiles) load_tile(pre, kv_lat, k_rope, kvoff, key0 + BN, key_last, tid);
+      f32x4 s = qk_tile<0>(qf, lane);
+      softmax_tile(s, o, st, c, key0 + BN > mask_from, key0, k_end, P, node, anc, lane);
+      pv_tile<0>(o, s, lane);
+      if (j + 1 >= n_tiles) break;
+      store_tile<1>(pre, tid);
+      __syncthreads();
+    }
+    {
+      const int key0 = k_begin + (j + 1) * BN;
+      if (j + 2 < n_tiles) load_tile(pre, kv_lat, k_rope, kvoff, key0 + BN, key_last, tid);
+      f32x4 s = qk_tile<1>(qf, lane);
+      softmax_tile(s, o, st, c, key0 + BN > mask_from, key0, k_end, P, node, anc, lane);
+      pv_tile<1>(o, s, lane);
+      if (j + 2 >= n_tiles) break;
+      store_tile<0>(pre, tid);
+      __syncthreads();
+    }
+  }
+
+  float l_tot = st.l + __shfl_xor(st.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv = 1.0f / l_tot;
+  const float lse = st.m * LN2 + logf(l_tot);
+  if (!row_ok) return;
+  float* out;
+  float* lse_out;
+  if (S == 1) {
+    out = p.out_lat + grow * DL;
+    lse_out = p.out_lse + grow;
+  } else {
+    out = p.part_o + ((int64_t)split * p.total_q * H + grow) * DL;
+    lse_out = p.part_lse + (int64_t)split * p.total_q * H + grow;
+  }
+#pragma unroll
+  for (int fb = 0; fb < 32; ++fb)
+    *(float4*)(out + fb * 16 + g * 4) =
+        make_float4(o[fb][0] * inv, o[fb][1] * inv, o[fb][2] * inv, o[fb][3] * inv);
+  if (g == 0) {
+    *lse_out = lse;
+    if (!(fabsf(lse) < INFINITY) && p.status) atomicOr(p.status, ST_NONFINITE);
+  }
+}
+
+}  // namespace
+
+int rows_per_block_f32() { return BM; }
+
+hipError_t launch_verify_f32(const VerifyParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.m_tiles * p.num_splits * p.batch;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_attn_f32_kernel, dim3((unsigned)blocks), dim3(NTHR), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kdt

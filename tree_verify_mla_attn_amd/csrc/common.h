@@ -1,0 +1,46 @@
+// Shared definitions of the gfx950 tree-verify MLA-absorb attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kdt {
+
+constexpr int DL = 512;          // latent dims (value vector and output)
+constexpr int DR = 64;           // rope dims (scores only)
+constexpr int DK = DL + DR;      // score contraction depth
+constexpr int MAX_QLEN = 65;     // draft budget 64 + root
+constexpr int MAX_REQUEST_KEYS = 1 << 24;  // prefix_len + q_len of one request
+constexpr float LN2 = 0.69314718055994530942f;
+
+// Status bits (mirrors include/kdtree_verify.h).
+constexpr int ST_BAD_QLEN = 1, ST_BAD_PREFIX = 2, ST_BAD_PARENT = 4, ST_OVERFLOW = 8,
+              ST_NONFINITE = 16;
+
+struct VerifyParams {
+  const void* q_lat;
+  const void* q_rope;
+  const void* kv_lat;
+  const void* k_rope;
+  const int32_t* prefix_len;
+  const int32_t* tree_parent;
+  const int32_t* q_len;
+  float* out_lat;    // [total_q, H, 512] (num_splits == 1)
+  float* out_lse;    // [total_q, H]
+  float* part_o;     // [num_splits, total_q*H, 512] (num_splits > 1)
+  float* part_lse;   // [num_splits, total_q*H]
+  int32_t* status;   // nullable
+  float scale_log2;  // scale * log2(e)
+  int32_t batch, num_heads, max_q_len, num_splits, m_tiles;
+  int64_t total_q, total_kv;
+};
+
+// Host-side launchers (defined in the .hip files).
+hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream);
+hipError_t launch_verify_f32(const VerifyParams& p, hipStream_t stream);
+hipError_t launch_lse_merge(const float* part_o, const float* part_lse, float* out_lat,
+                            float* out_lse, int64_t rows, int32_t num_splits, hipStream_t stream);
+int rows_per_block_bf16();
+int rows_per_block_f32();
+
+}  // namespace kdt

@@ -39,15 +39,15 @@ LOGIT_STD = 2.0
 # --------------------------------------------------------------------------- bf16
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round-to-nearest-even); return the raw
-    16-bit patterns as uint16.  NaN stays NaN (quiet), infinities stay infinite."""
+    16-bit patterns as uint16.  NaN stays NaN (quiet), infinities stay infinite.
+    (uint32 arithmetic cannot wrap: the largest non-NaN pattern is 0xFF800000.)"""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
+    u = f.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    out = ((u + (np.uint32(0x7FFF) + lsb)) >> np.uint32(16)).astype(np.uint16)
     is_nan = np.isnan(f)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    out = rounded.astype(np.uint16)
     if is_nan.any():
-        out[is_nan] = ((u[is_nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
+        out[is_nan] = ((u[is_nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return out
 
 
@@ -286,3 +286,21 @@ def config_inputs(cfg: int, num_splits: Optional[int] = None) -> VerifyInputs:
     return make_inputs(rng, num_heads=c["heads"], prefix_lens=prefix, parents=parents,
                        dtype=c["dtype"], num_splits=num_splits or c["num_splits"],
                        name=c["name"])
+
+
+def device_tensors(inp: VerifyInputs, device="cuda"):
+    """Copy a VerifyInputs batch to torch tensors on ``device`` (bf16 bit-exact)."""
+    import torch
+
+    def t(x):
+        if inp.dtype == "bf16":
+            bits = bf16_bits(x).view(np.int16)
+            return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+
+    def ti(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
+
+    return dict(q_lat=t(inp.q_lat), q_rope=t(inp.q_rope), kv_lat=t(inp.kv_lat),
+                k_rope=t(inp.k_rope), prefix_len=ti(inp.prefix_len),
+                tree_parent=ti(inp.tree_parent), q_len=ti(inp.q_len))
