@@ -95,10 +95,10 @@ def main():
     call = B.VerifyAttn()
     out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)
-    ws = None
-    if splits > 1:
-        ws = torch.empty(B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.num_heads, splits),
-                         dtype=torch.uint8, device=dev)
+    ws_bytes = B.kdtree_verify_attn_workspace_bytes(
+        inp.total_q, inp.total_kv, inp.batch, inp.num_heads, splits,
+        B.KDTREE_DTYPE_BF16 if inp.dtype == "bf16" else B.KDTREE_DTYPE_FP32)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     argv = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
             d["q_len"], inp.scale)

@@ -68,7 +68,7 @@ extern "C" {
 #define KDTREE_ERR_QLEN (-3)        /* max_q_len outside [1, KDTREE_MAX_QLEN] */
 #define KDTREE_ERR_DTYPE (-4)       /* dtype not FP32 / BF16 */
 #define KDTREE_ERR_SPLITS (-5)      /* num_splits < 1 or > 256, or workspace NULL /
-                                       too small for num_splits > 1 */
+                                       smaller than kdtree_verify_attn_workspace_bytes */
 #define KDTREE_ERR_SCALE (-6)       /* scale not finite */
 #define KDTREE_ERR_LAUNCH (-7)      /* HIP launch failure */
 
@@ -83,10 +83,15 @@ extern "C" {
 /* MAX_QLEN (65). */
 int32_t kdtree_max_qlen(void);
 
-/* Workspace bytes kdtree_verify_attn needs: 0 for num_splits == 1, otherwise
- * num_splits * total_q * num_heads * (512 + 1) * 4 rounded up to 256 bytes (the
- * split partial outputs and their log-sum-exps).  Returns 0 for invalid sizes. */
-size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_splits);
+/* Workspace bytes kdtree_verify_attn needs (0 = none).  Returns 0 for invalid sizes.
+ * Regions (each rounded up to 256 bytes):
+ *   bf16 inputs: the request schedule (batch int32) and fp16 copies of the latent rows,
+ *     feature-major in 32-key tiles, both written by a pre-pass of the same call:
+ *     batch * 4 and (total_kv / 32 + batch + 1) * 32 KB bytes;
+ *   num_splits > 1: split partial outputs num_splits * total_q * num_heads * 512 * 4
+ *     bytes and their log-sum-exps num_splits * total_q * num_heads * 4 bytes. */
+size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int32_t batch,
+                                          int32_t num_heads, int32_t num_splits, int32_t dtype);
 
 /*
  * Tree-verify MLA-absorb attention (see the top of this file).
@@ -108,12 +113,14 @@ size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int32_t num_heads, in
  *                a request whose packed offsets exceed them is skipped and flagged.
  *   dtype        KDTREE_DTYPE_FP32 or KDTREE_DTYPE_BF16 (all four inputs).
  *   num_splits   split-KV factor (1..256).  With S > 1 each request's prefix is cut
- *                into S chunks of ceil(P/S) keys (the tail goes with the last chunk);
+ *                into S chunks of ceil(P/S) keys rounded up to a multiple of 32 (the
+ *                tail goes with the last chunk; trailing chunks may be empty);
  *                each chunk's partial output + lse is written to `workspace` and a
  *                merge pass combines them ("The Milestone Commit ...", section "What
  *                to defer": flash partial outputs merged for long prefixes).
- *   workspace    device buffer of kdtree_verify_attn_workspace_bytes(...) bytes
- *                (may be NULL when num_splits == 1).
+ *   workspace    device buffer of at least kdtree_verify_attn_workspace_bytes(...)
+ *                bytes (may be NULL when that is 0: fp32 inputs with num_splits == 1).
+ *                Its contents are scratch; calls sharing a workspace must not overlap.
  *   status       optional device int32; the kernels OR KDTREE_STATUS_* bits into it
  *                on malformed device inputs (the caller zeroes it).  Rows of a
  *                flagged request are left unwritten.

@@ -42,15 +42,22 @@ def test_header_constants_match_binding():
 
 
 def test_workspace_bytes():
-    assert B.kdtree_verify_attn_workspace_bytes(100, 64, 1) == 0
-    n = B.kdtree_verify_attn_workspace_bytes(260, 64, 16)
-    rows = 260 * 64
-    o_bytes = -(-16 * rows * 512 * 4 // 256) * 256
-    assert n == -(-(o_bytes + 16 * rows * 4) // 256) * 256
-    assert n % 256 == 0
-    assert B.kdtree_verify_attn_workspace_bytes(0, 64, 2) == 0
-    assert B.kdtree_verify_attn_workspace_bytes(10, 64, 0) == 0
-    assert B.kdtree_verify_attn_workspace_bytes(10, 64, 257) == 0
+    def up(x):
+        return -(-x // 256) * 256
+    # fp32, one split: nothing
+    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 0) == 0
+    # bf16, one split: the fp16 V^T tiles only
+    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 1) == up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768)
+    # bf16, 16 splits: tiles + partial outputs + partial lse
+    tq, tkv, b, h, s = 260, 131332, 4, 64, 16
+    rows = tq * h
+    want = up(b * 4) + up((tkv // 32 + b + 1) * 32768) + up(s * rows * 512 * 4) + up(s * rows * 4)
+    assert B.kdtree_verify_attn_workspace_bytes(tq, tkv, b, h, s, 1) == want
+    # fp32, splits: partials only
+    assert B.kdtree_verify_attn_workspace_bytes(tq, tkv, b, h, s, 0) == up(s * rows * 512 * 4) + up(s * rows * 4)
+    for bad in [(0, 10, 1, 64, 2, 1), (10, 10, 1, 64, 0, 1), (10, 10, 1, 64, 257, 1),
+                (10, 10, 1, 64, 2, 3), (10, 10, 0, 64, 2, 1)]:
+        assert B.kdtree_verify_attn_workspace_bytes(*bad) == 0
 
 
 def _call(**kw):
@@ -72,7 +79,7 @@ def test_null_pointer_rejected(field):
     (dict(batch=0), -2), (dict(num_heads=0), -2), (dict(total_q=1), -2),
     (dict(total_kv=10), -2), (dict(max_q_len=0), -3), (dict(max_q_len=66), -3),
     (dict(dtype=2), -4), (dict(dtype=-1), -4), (dict(num_splits=0), -5),
-    (dict(num_splits=300), -5), (dict(num_splits=4), -5),
+    (dict(num_splits=300), -5), (dict(num_splits=4), -5), (dict(dtype=1, num_splits=1), -5),
     (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), -5),
     (dict(scale=float("nan")), -6), (dict(scale=float("inf")), -6),
 ])

@@ -217,7 +217,8 @@ def test_hip_graph_capture_replays(dev):
     call = B.VerifyAttn()
     out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)
-    ws = torch.empty(B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.num_heads, 4),
+    ws = torch.empty(B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.total_kv, inp.batch,
+                                                          inp.num_heads, 4, B.KDTREE_DTYPE_BF16),
                      dtype=torch.uint8, device=dev)
     args = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
             d["q_len"], inp.scale)

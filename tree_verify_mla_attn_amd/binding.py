@@ -50,7 +50,7 @@ def load_library():
     lib.kdtree_max_qlen.restype = i32
     lib.kdtree_max_qlen.argtypes = []
     lib.kdtree_verify_attn_workspace_bytes.restype = sz
-    lib.kdtree_verify_attn_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.kdtree_verify_attn_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
     lib.kdtree_verify_attn.restype = i32
     lib.kdtree_verify_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                        i32, i32, i32, i64, i64, i32, i32, vp, sz, vp]
@@ -63,8 +63,10 @@ def kdtree_max_qlen() -> int:
     return int(load_library().kdtree_max_qlen())
 
 
-def kdtree_verify_attn_workspace_bytes(total_q: int, num_heads: int, num_splits: int) -> int:
-    return int(load_library().kdtree_verify_attn_workspace_bytes(total_q, num_heads, num_splits))
+def kdtree_verify_attn_workspace_bytes(total_q: int, total_kv: int, batch: int, num_heads: int,
+                                       num_splits: int, dtype: int) -> int:
+    return int(load_library().kdtree_verify_attn_workspace_bytes(total_q, total_kv, batch,
+                                                                 num_heads, num_splits, dtype))
 
 
 def kdtree_verify_attn(q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
@@ -138,20 +140,20 @@ class VerifyAttn:
                 or tuple(out_lat.shape) != (total_q, h, D_LATENT) or tuple(out_lse.shape) != (total_q, h) \
                 or not out_lat.is_contiguous() or not out_lse.is_contiguous():
             raise ValueError("out_lat / out_lse must be contiguous float32 [total_q, H, 512] / [total_q, H]")
-        need = kdtree_verify_attn_workspace_bytes(total_q, h, num_splits)
-        if num_splits > 1:
-            if workspace is None or workspace.numel() * workspace.element_size() < need:
-                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        ws_ptr = workspace.data_ptr() if (workspace is not None and num_splits > 1) else 0
+        total_kv = int(kv_lat.shape[0])
+        dt = KDTREE_DTYPE_BF16 if dtype == torch.bfloat16 else KDTREE_DTYPE_FP32
+        need = kdtree_verify_attn_workspace_bytes(total_q, total_kv, batch, h, int(num_splits), dt)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() if (workspace is not None and need) else 0
         ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = kdtree_verify_attn(
             q_lat.data_ptr(), q_rope.data_ptr(), kv_lat.data_ptr(), k_rope.data_ptr(),
             prefix_len.data_ptr(), tree_parent.data_ptr(), q_len.data_ptr(), float(scale),
             out_lat.data_ptr(), out_lse.data_ptr(), stream, batch, h, int(max_q_len), total_q,
-            int(kv_lat.shape[0]),
-            KDTREE_DTYPE_BF16 if dtype == torch.bfloat16 else KDTREE_DTYPE_FP32,
-            int(num_splits), ws_ptr, ws_bytes, status.data_ptr() if status is not None else 0)
+            total_kv, dt, int(num_splits), ws_ptr, ws_bytes,
+            status.data_ptr() if status is not None else 0)
         if rc != 0:
             raise RuntimeError(f"kdtree_verify_attn failed: {rc} ({ERRORS.get(rc, '?')})")
         return out_lat, out_lse

@@ -16,9 +16,8 @@
 //     raised when a tile beats it by more than 2^8);
 //   * O^T += V^T P^T: fp16 MFMA 32x32x16 with P in fp16 (bf16 P is too coarse for a
 //     2e-3 relative bound) against an fp16, feature-major copy of the latent tile.
-// KV tiles (32 keys x 576 bf16) arrive by 16-byte global->LDS DMA into a swizzled,
-// double-buffered layout; each tile's latent part is converted once per workgroup to
-// the fp16 feature-major layout the PV contraction reads.
+// KV tiles (32 keys x 576 bf16) and the matching fp16 V^T tiles (converted once per
+// call by the pre-pass) arrive by 16-byte global->LDS DMA into double-buffered LDS.
 #include "common.h"
 
 namespace kdt {
@@ -41,7 +40,9 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 //   K latent [32 keys][64 chunks + 1 pad]: chunk c of key k at slot k*65 + c (the pad
 //            staggers rows across banks and keeps every k-step a constant offset);
 //   K rope   [32 keys][8 chunks]:  chunk c of key k at slot k*8 + (c ^ rswz(k));
-//   V^T fp16 [512 features][4 chunks of 8 keys]: chunk q of feature f at f*4 + (q ^ vswz(f)).
+//   V^T fp16 [512 features][4 chunks of 8 keys]: chunk q of feature f at
+//            vt_slot(f, q) = f*4 + (q ^ ((f >> 2) & 3)) -- the pre-pass's tile image; the
+//            swizzle keeps the PV reads (32 consecutive features) bank-conflict free.
 constexpr int KLAT_ROW = 65;
 constexpr int KLAT_U4 = BN * KLAT_ROW, KROPE_U4 = BN * 8, VT_U4 = DL * 4;
 // Separate objects per stage: the compiler's wait-count insertion can then tell that a
@@ -54,11 +55,11 @@ __shared__ __attribute__((aligned(1024))) u32x4 sKrope1[KROPE_U4];
 __shared__ __attribute__((aligned(1024))) u32x4 sVt0[VT_U4];
 __shared__ __attribute__((aligned(1024))) u32x4 sVt1[VT_U4];
 __shared__ int32_t sParent[MAX_QLEN];
-__shared__ int64_t sRed[2 * 4];
+__shared__ int64_t sRed[3 * 4];
 __shared__ int32_t sFlag;
 
 __device__ __forceinline__ int rswz(int k) { return (k ^ (k >> 3)) & 7; }
-__device__ __forceinline__ int vswz(int f) { return ((f >> 1) ^ (f >> 2)) & 3; }
+__device__ __forceinline__ int vt_slot(int f, int q) { return f * 4 + (q ^ ((f >> 2) & 3)); }
 
 template <int STAGE> __device__ __forceinline__ u32x4* klat() { return STAGE ? sKlat1 : sKlat0; }
 template <int STAGE> __device__ __forceinline__ u32x4* krope() { return STAGE ? sKrope1 : sKrope0; }
@@ -95,41 +96,15 @@ __device__ __forceinline__ void issue_tile(const char* kv_lat_req, const char* k
   }
 }
 
-// Convert the latent part of a stage to fp16 feature-major V^T.  Thread t handles
-// feature group fg = t/4 (features 8fg..8fg+7) and key chunk q = t%4: keys
-// {b..b+3, b+8..b+11} with b = 16(q/2) + 4(q%2), in the order the PV MFMA's k slots use.
-// Features are done in two halves of 4 (8-byte LDS reads) to keep few VGPRs live.
+// DMA of the pre-converted V^T tile `tile` into a stage (wave w moves 1 KB blocks
+// 8w..8w+7 of the 32 KB tile image).
 template <int STAGE>
-__device__ __forceinline__ void convert_tile(int tid) {
-  const u32x4* kl = klat<STAGE>();
-  u32x4* v = vt<STAGE>();
-  const int q = tid & 3;
-  const int fg = tid >> 2;
-  const int base = 16 * (q >> 1) + 4 * (q & 1);
+__device__ __forceinline__ void issue_vt(const char* vt_req, int tile, int wave, int lane) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    uint2 w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = base + (e >> 2) * 8 + (e & 3);
-      w[e] = ((const uint2*)(kl + k * KLAT_ROW + fg))[half];
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = half * 4 + jj;
-      u32x4 o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const unsigned a = (jj >> 1) ? w[2 * d].y : w[2 * d].x;
-        const unsigned b = (jj >> 1) ? w[2 * d + 1].y : w[2 * d + 1].x;
-        const float fa = __uint_as_float((jj & 1) ? (a & 0xffff0000u) : (a << 16));
-        const float fb = __uint_as_float((jj & 1) ? (b & 0xffff0000u) : (b << 16));
-        fp16x2 h = __builtin_amdgcn_cvt_pkrtz(fa, fb);
-        o[d] = __builtin_bit_cast(unsigned, h);
-      }
-      const int f = fg * 8 + j;
-      v[f * 4 + (q ^ vswz(f))] = o;
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
+    dma16(vt_req + (int64_t)tile * VT_TILE_BYTES + blk * 1024, (unsigned)lane * 16u,
+          vt<STAGE>() + blk * 64);
   }
 }
 
@@ -157,6 +132,53 @@ __device__ __forceinline__ f32x16 qk_tile(const u32x4 (&qf)[36], int lane) {
   return s;
 }
 
+// Scores of the next tile fused with the copies that must be in flight meanwhile: the
+// K tile j+2 into stage SC and the V^T tile j+1 into stage SN.  One 1 KB DMA is
+// spliced after every two score MFMAs, so the copy engine's queue drains in the shadow
+// of the matrix pipe instead of stalling the wave in one burst.
+template <int SC, int SN>
+__device__ __forceinline__ f32x16 qk_dma(const u32x4 (&qf)[36], int lane, const char* kv_lat_req,
+                                         const char* k_rope_req, const char* vt_req, int k_key0,
+                                         int key_last, int vt_tile, int wave) {
+  const u32x4* kl = klat<SN>();
+  const u32x4* kr = krope<SN>();
+  const int key = lane & 31, h = lane >> 5;
+  auto frag = [&](int ks) -> u32x4 {
+    const int c = 2 * ks + h;
+    return ks < 32 ? kl[key * KLAT_ROW + c] : kr[key * 8 + ((c - 64) ^ rswz(key))];
+  };
+  u32x4 a[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = frag(i);
+  f32x16 s = {};
+  int dl = lane;
+  asm volatile("" : "+v"(dl));  // per-tile lane offsets, not hoisted out of the KV loop
+  auto dma = [&](int n) {
+    if (n < 8) {          // K latent row wave*8 + n
+      const int kk = wave * 8 + n;
+      const int k = __builtin_amdgcn_readfirstlane(min(k_key0 + kk, key_last));
+      dma16(kv_lat_req + (int64_t)k * (DL * 2), (unsigned)dl * 16u, klat<SC>() + kk * KLAT_ROW);
+    } else if (n == 8) {  // K rope rows wave*8 .. +7
+      const int kk = wave * 8 + (dl >> 3);
+      const int k = min(k_key0 + kk, key_last);
+      dma16(k_rope_req, (unsigned)k * (DR * 2) + (unsigned)((dl & 7) ^ rswz(kk)) * 16u,
+            krope<SC>() + wave * 64);
+    } else {              // V^T tile: 1 KB blocks wave*8 + (n - 9)
+      const int blk = wave * 8 + (n - 9);
+      dma16(vt_req + (int64_t)vt_tile * VT_TILE_BYTES + blk * 1024, (unsigned)dl * 16u,
+            vt<SN>() + blk * 64);
+    }
+  };
+#pragma unroll
+  for (int ks = 0; ks < 36; ++ks) {
+    if (ks + 4 < 36) a[(ks + 4) & 7] = frag(ks + 4);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks & 7]),
+                                                __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
+    if ((ks & 1) && (ks >> 1) < 17) dma(ks >> 1);
+  }
+  return s;
+}
+
 // O^T += V^T P^T for one 32-key tile: 16 feature blocks x 2 key steps of fp16 MFMA
 // 32x32x16.  Written as one asm block so that the 16 output accumulators stay in the
 // AGPR file (256 registers) across the KV loop while Q, S and P use VGPRs.  V^T
@@ -168,10 +190,10 @@ __device__ __forceinline__ f32x16 qk_tile(const u32x4 (&qf)[36], int lane) {
 template <int STAGE>
 __device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const f16x8 (&pk)[2], int lane) {
   const int fl = lane & 31, h = lane >> 5;
-  const int sw = vswz(fl);
+  // feature 32*fb + fl lives at byte vt_slot(fl, .)*16 + fb*2048
   const unsigned base = (unsigned)(size_t)(LDS_AS void*)vt<STAGE>();
-  const unsigned v0 = base + (unsigned)((fl * 4 + ((0 + h) ^ sw)) * 16);
-  const unsigned v1 = base + (unsigned)((fl * 4 + ((2 + h) ^ sw)) * 16);
+  const unsigned v0 = base + (unsigned)(vt_slot(fl, 0 + h) * 16);
+  const unsigned v1 = base + (unsigned)(vt_slot(fl, 2 + h) * 16);
   u32x4 t0, t1, t2, t3, t4, t5, t6, t7;
   asm volatile(
       "s_nop 4\n"
@@ -281,7 +303,17 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const f16x8 (&pk)[2], i
       : "memory");
 }
 
-__device__ __forceinline__ float lane_swap32(float x) { return __shfl_xor(x, 32); }
+// max / sum of x over the lane pair (l, l ^ 32) that shares a query row, without an
+// LDS round trip: v_permlane32_swap exchanges the upper half of one copy with the lower
+// half of the other, so every lane ends up with both values of its pair.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 
 // The output accumulators live in AGPRs for the whole kernel.  Any VALU arithmetic on
 // them goes through an explicit copy to fresh VGPRs (the empty asm makes the copy a
@@ -313,15 +345,17 @@ struct RowState {
 };
 
 // Visibility of keys [key0, key0 + 32) for this lane's row as a bit mask (bit kt set =
-// key key0 + kt visible): keys at or past key_end are out of range; prefix keys are
+// key key0 + kt visible): keys outside [key_begin, key_end) are out of range; prefix keys are
 // visible; tail key P + j is visible iff node j is an ancestor-or-self of the row's
 // node ("Strategic Pivots ...", section "The Message": tree visibility mask).  `anc`
 // holds bits 0..63 of the ancestor-or-self set; node 64 can only be its own ancestor.
-__device__ __forceinline__ uint32_t tile_visibility(int key0, int key_end, int prefix, int node,
-                                                    uint64_t anc) {
+__device__ __forceinline__ uint32_t tile_visibility(int key0, int key_begin, int key_end,
+                                                    int prefix, int node, uint64_t anc) {
   uint32_t vis = 0xffffffffu;
   const int nvalid = key_end - key0;
   if (nvalid < 32) vis = nvalid <= 0 ? 0u : (0xffffffffu >> (32 - nvalid));
+  const int nskip = key_begin - key0;  // keys before this split's range
+  if (nskip > 0) vis &= nskip >= 32 ? 0u : (0xffffffffu << nskip);
   const int t0 = prefix - key0;  // tile index of tail node 0
   if (t0 < 32) {
     const uint32_t tail_pos = t0 <= 0 ? 0xffffffffu : (0xffffffffu << t0);
@@ -350,7 +384,7 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, lane_swap32(mx));
+  mx = pair_max(mx);
   // Lazy rescale: the running max only moves when this tile beats it by more than
   // 2^RESCALE_THRESHOLD; the caller then scales O by `alpha` (rare after the first tile).
   const bool need = mx > st.m + RESCALE_THRESHOLD;  // also true when st.m == -inf
@@ -386,7 +420,10 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
 struct TileLoop {
   const char* kv_lat;
   const char* k_rope;
-  int k_begin, k_end, key_last, n_tiles, mask_from, prefix, node;
+  const char* vt;  // this split's first V^T tile
+  int k_begin;     // first key of tile 0 (32-aligned)
+  int k_first;     // first key of the split's range (>= k_begin)
+  int k_end, key_last, n_tiles, mask_from, prefix, node;
   uint64_t anc;
   float c;
   int tid, wave, lane;
@@ -395,8 +432,9 @@ struct TileLoop {
   __device__ __forceinline__ void iteration(int j, f32x16& s_cur, f32x16 (&o)[16], RowState& st,
                                             const u32x4 (&qf)[36]) const {
     const int key0 = k_begin + j * BN;
-    const bool masked = key0 + BN > mask_from;
-    const uint32_t vis = masked ? tile_visibility(key0, k_end, prefix, node, anc) : 0xffffffffu;
+    const bool masked = key0 < k_first || key0 + BN > mask_from;
+    const uint32_t vis = masked ? tile_visibility(key0, k_first, k_end, prefix, node, anc)
+                                : 0xffffffffu;
     f16x8 pk[2];
     softmax_tile(s_cur, pk, st, c, masked, vis, lane);
     if (__builtin_expect(st.rescale, 0)) {
@@ -405,9 +443,10 @@ struct TileLoop {
     }
     const bool more = j + 1 < n_tiles;
     if (more) {
-      if (j + 2 < n_tiles) issue_tile<STAGE>(kv_lat, k_rope, key0 + 2 * BN, key_last, wave, lane);
-      s_cur = qk_tile<STAGE ^ 1>(qf, lane);
-      convert_tile<STAGE ^ 1>(tid);
+      // Past the last tile the DMA is clamped to the last key: a harmless refill of a
+      // buffer nobody reads any more.
+      s_cur = qk_dma<STAGE, STAGE ^ 1>(qf, lane, kv_lat, k_rope, vt, key0 + 2 * BN, key_last,
+                                       j + 1, wave);
     }
     pv_tile<STAGE>(o, pk, lane);
     if (more) {
@@ -424,14 +463,22 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const int h = lane >> 5;
 
   // ---- which (request, split, row tile) ------------------------------------------
-  int bid = blockIdx.x;
-  const int mt = bid % p.m_tiles;
-  bid /= p.m_tiles;
-  const int split = bid % p.num_splits;
-  const int b = bid / p.num_splits;
+  // Workgroup i runs on XCD i % 8.  Work comes in groups of m_tiles row tiles that share
+  // one (request, split) KV range; groups are ranked by request (longest KV first, from
+  // the pre-pass) then split, and XCD x takes groups x, x+8, x+16, ...: every XCD gets an
+  // even, longest-first share, and the row tiles of a group share that XCD's L2.
+  const int slot = blockIdx.x / NUM_XCD;
+  const int grank = (int)(blockIdx.x % NUM_XCD) + NUM_XCD * (slot / p.m_tiles);
+  if (grank >= p.batch * p.num_splits) return;
+  const int mt = slot % p.m_tiles;
+  const int rank = grank / p.num_splits;
+  const int split = grank % p.num_splits;
+  int b = p.order ? p.order[rank] : rank;
+  if (b < 0 || b >= p.batch) b = rank;
+  b = __builtin_amdgcn_readfirstlane(b);
 
   // ---- packed offsets: exclusive prefix sums over earlier requests ---------------
-  int64_t qoff = 0, kvoff = 0;
+  int64_t qoff = 0, kvoff = 0, tbase = 0;
   int bad = 0;
   for (int i = tid; i < b; i += NTHR) {
     const int t = p.q_len[i], pl = p.prefix_len[i];
@@ -439,10 +486,12 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
     bad |= pl < 0 ? ST_BAD_PREFIX : 0;
     qoff += t;
     kvoff += (int64_t)pl + t;
+    tbase += ((int64_t)pl + t + VT_TILE_KEYS - 1) / VT_TILE_KEYS;
   }
   for (int off = 32; off > 0; off >>= 1) {
     qoff += __shfl_xor(qoff, off);
     kvoff += __shfl_xor(kvoff, off);
+    tbase += __shfl_xor(tbase, off);
     bad |= __shfl_xor(bad, off);
   }
   if (tid == 0) sFlag = 0;
@@ -450,11 +499,13 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   if (lane == 0) {
     sRed[wave] = qoff;
     sRed[4 + wave] = kvoff;
+    sRed[8 + wave] = tbase;
     if (bad) atomicOr(&sFlag, bad);
   }
   __syncthreads();
   qoff = uniform64(sRed[0] + sRed[1] + sRed[2] + sRed[3]);
   kvoff = uniform64(sRed[4] + sRed[5] + sRed[6] + sRed[7]);
+  tbase = uniform64(sRed[8] + sRed[9] + sRed[10] + sRed[11]);
   const int T = p.q_len[b];
   const int P = p.prefix_len[b];
   int flag = __builtin_amdgcn_readfirstlane(sFlag);
@@ -503,7 +554,8 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const int S = p.num_splits;
   int k_begin, k_end;
   {
-    const int chunk = (P + S - 1) / S;
+    // chunks of whole 32-key tiles, so every split starts on a V^T tile boundary
+    const int chunk = ((P + S - 1) / S + BN - 1) / BN * BN;
     k_begin = min(P, split * chunk);
     k_end = (split == S - 1) ? P + T : min(P, (split + 1) * chunk);
   }
@@ -532,6 +584,11 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
 
   const char* kv_lat = (const char*)p.kv_lat + kvoff * (DL * 2);  // this request's rows
   const char* k_rope = (const char*)p.k_rope + kvoff * (DR * 2);
+  // Tiles are 32-aligned in the request's key stream (the V^T tiles are); a split whose
+  // range starts mid-tile (only the last split, when the prefix is short) masks the keys
+  // before its range.
+  const int k_first = k_begin;
+  k_begin &= ~(BN - 1);
   const int key_last = k_end - 1;
   const int n_tiles = (k_end - k_begin + BN - 1) / BN;
   const int mask_from = min(P, k_end);  // tiles ending at or before this key are unmasked
@@ -545,17 +602,22 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   // Pipeline: iteration j runs the softmax and PV of tile j while the scores of tile
   // j+1 are computed and its V^T converted; the DMA of tile j+2 is in flight.  One
   // barrier per tile.  Stage j&1 holds K(j) / V^T(j).
+  if (tbase + (P + T + BN - 1) / BN > p.vt_tiles) {  // cannot happen for valid offsets
+    if (tid == 0 && p.status) atomicOr(p.status, ST_OVERFLOW);
+    return;
+  }
+  const char* vt_split = (const char*)p.vt + (tbase + k_begin / BN) * VT_TILE_BYTES;
   issue_tile<0>(kv_lat, k_rope, k_begin, key_last, wave, lane);
+  issue_vt<0>(vt_split, 0, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  convert_tile<0>(tid);
   if (n_tiles > 1) issue_tile<1>(kv_lat, k_rope, k_begin + BN, key_last, wave, lane);
   f32x16 s_cur = qk_tile<0>(qf, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  TileLoop tl{kv_lat, k_rope, k_begin, k_end, key_last, n_tiles, mask_from, P, node, anc, c,
-              tid, wave, lane};
+  TileLoop tl{kv_lat, k_rope, vt_split, k_begin, k_first, k_end, key_last, n_tiles, mask_from,
+              P, node, anc, c, tid, wave, lane};
   for (int j = 0; j < n_tiles; j += 2) {
     tl.iteration<0>(j, s_cur, o, st, qf);
     if (j + 1 >= n_tiles) break;
@@ -563,7 +625,7 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   }
 
   // ---- finalize -------------------------------------------------------------------
-  const float l_tot = st.l + lane_swap32(st.l);
+  const float l_tot = pair_sum(st.l);
   const float inv = 1.0f / l_tot;
   const float lse = st.m * LN2 + logf(l_tot);
   if (!row_ok) return;
@@ -597,7 +659,8 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
 int rows_per_block_bf16() { return BM; }
 
 hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.m_tiles * p.num_splits * p.batch;
+  const int64_t groups = (int64_t)p.batch * p.num_splits;
+  const int64_t blocks = (int64_t)NUM_XCD * ((groups + NUM_XCD - 1) / NUM_XCD) * p.m_tiles;
   if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(verify_attn_bf16_kernel, dim3((unsigned)blocks), dim3(NTHR), 0, stream, p);
   return hipGetLastError();

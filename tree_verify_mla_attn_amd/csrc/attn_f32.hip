@@ -216,7 +216,7 @@ void verify_attn_f32_kernel(VerifyParams p) {
   const int S = p.num_splits;
   int k_begin, k_end;
   {
-    const int chunk = (P + S - 1) / S;
+    const int chunk = ((P + S - 1) / S + 31) / 32 * 32;  // whole 32-key tiles, as the bf16 path
     k_begin = min(P, split * chunk);
     k_end = (split == S - 1) ? P + T : min(P, (split + 1) * chunk);
   }

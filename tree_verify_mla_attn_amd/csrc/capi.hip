@@ -13,20 +13,28 @@ constexpr int32_t kMaxSplits = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Bytes of the per-split partial outputs and log-sum-exps; 0 when not needed.
-bool workspace_layout(int64_t total_q, int32_t num_heads, int32_t num_splits, size_t* o_bytes,
-                      size_t* total) {
-  if (total_q < 1 || num_heads < 1 || num_splits < 1 || num_splits > kMaxSplits) return false;
-  if (num_splits == 1) {
-    *o_bytes = 0;
-    *total = 0;
-    return true;
-  }
-  const double est = (double)num_splits * (double)total_q * num_heads * (kdt::DL + 1) * 4.0;
-  if (est > 9.0e18) return false;
+struct WorkspaceLayout {
+  size_t order_bytes, vt_bytes, part_o_bytes, part_lse_bytes, total;
+  int64_t vt_tiles;
+};
+
+// Workspace: [request order + fp16 V^T tiles (bf16 inputs)] [split partial outputs]
+// [split lse], each
+// region 256-byte aligned.  V^T tiles: one 32 KB tile per 32 keys of every request,
+// bounded by total_kv / 32 + batch (each request adds at most one partial tile).
+bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t num_heads,
+                      int32_t num_splits, int32_t dtype, WorkspaceLayout* w) {
+  if (total_q < 1 || total_kv < 1 || batch < 1 || num_heads < 1 || num_splits < 1 ||
+      num_splits > kMaxSplits || (dtype != KDTREE_DTYPE_FP32 && dtype != KDTREE_DTYPE_BF16))
+    return false;
+  if (total_q > ((int64_t)1 << 40) || total_kv > ((int64_t)1 << 40)) return false;
+  w->vt_tiles = dtype == KDTREE_DTYPE_BF16 ? total_kv / kdt::VT_TILE_KEYS + batch + 1 : 0;
+  w->order_bytes = dtype == KDTREE_DTYPE_BF16 ? round_up((size_t)batch * 4, 256) : 0;
+  w->vt_bytes = round_up((size_t)w->vt_tiles * (size_t)kdt::VT_TILE_BYTES, 256);
   const size_t rows = (size_t)total_q * (size_t)num_heads;
-  *o_bytes = round_up((size_t)num_splits * rows * kdt::DL * sizeof(float), 256);
-  *total = round_up(*o_bytes + (size_t)num_splits * rows * sizeof(float), 256);
+  w->part_o_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * kdt::DL * sizeof(float), 256) : 0;
+  w->part_lse_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * sizeof(float), 256) : 0;
+  w->total = w->order_bytes + w->vt_bytes + w->part_o_bytes + w->part_lse_bytes;
   return true;
 }
 
@@ -36,10 +44,11 @@ extern "C" {
 
 int32_t kdtree_max_qlen(void) { return KDTREE_MAX_QLEN; }
 
-size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int32_t num_heads, int32_t num_splits) {
-  size_t o_bytes = 0, total = 0;
-  if (!workspace_layout(total_q, num_heads, num_splits, &o_bytes, &total)) return 0;
-  return total;
+size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int32_t batch,
+                                          int32_t num_heads, int32_t num_splits, int32_t dtype) {
+  WorkspaceLayout w;
+  if (!workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &w)) return 0;
+  return w.total;
 }
 
 int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv_lat,
@@ -60,9 +69,10 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
     return KDTREE_ERR_SHAPE;
   if (dtype != KDTREE_DTYPE_FP32 && dtype != KDTREE_DTYPE_BF16) return KDTREE_ERR_DTYPE;
   if (!isfinite(scale)) return KDTREE_ERR_SCALE;
-  size_t o_bytes = 0, need = 0;
-  if (!workspace_layout(total_q, num_heads, num_splits, &o_bytes, &need)) return KDTREE_ERR_SPLITS;
-  if (num_splits > 1 && (!workspace || workspace_bytes < need)) return KDTREE_ERR_SPLITS;
+  WorkspaceLayout w;
+  if (!workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &w))
+    return KDTREE_ERR_SPLITS;
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return KDTREE_ERR_SPLITS;
 
   kdt::VerifyParams p;
   p.q_lat = q_lat;
@@ -74,8 +84,13 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
   p.q_len = q_len;
   p.out_lat = out_lat;
   p.out_lse = out_lse;
-  p.part_o = num_splits > 1 ? (float*)workspace : nullptr;
-  p.part_lse = num_splits > 1 ? (float*)((char*)workspace + o_bytes) : nullptr;
+  char* ws = (char*)workspace;
+  p.order = w.order_bytes ? (int32_t*)ws : nullptr;
+  p.vt = w.vt_bytes ? ws + w.order_bytes : nullptr;
+  p.vt_tiles = w.vt_tiles;
+  p.part_o = num_splits > 1 ? (float*)(ws + w.order_bytes + w.vt_bytes) : nullptr;
+  p.part_lse =
+      num_splits > 1 ? (float*)(ws + w.order_bytes + w.vt_bytes + w.part_o_bytes) : nullptr;
   p.status = status;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.batch = batch;
@@ -89,7 +104,14 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
   if ((int64_t)p.m_tiles * num_splits * batch > 0x7fffffff) return KDTREE_ERR_SHAPE;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == KDTREE_DTYPE_BF16 ? kdt::launch_verify_bf16(p, s) : kdt::launch_verify_f32(p, s);
+  hipError_t e;
+  if (dtype == KDTREE_DTYPE_BF16) {
+    e = kdt::launch_vt_prepass(p, w.vt_tiles, s);
+    if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
+    e = kdt::launch_verify_bf16(p, s);
+  } else {
+    e = kdt::launch_verify_f32(p, s);
+  }
   if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
   if (num_splits > 1) {
     e = kdt::launch_lse_merge(p.part_o, p.part_lse, out_lat, out_lse, total_q * num_heads,
