@@ -8,8 +8,9 @@ resident in HBM before timing starts.
 
 Prints ONE JSON line (rank 0):
   value      = algorithmic TFLOP/s (2*(576+512) flops per visible (row, key) pair)
-  roofline   = the attention kernel vs the bf16 dense MFMA peak (2.5 PFLOP/s), from
-               HIP events on the launch stream over the timed region
+  roofline   = the attention kernel vs the dense MFMA peak of its dtype (bf16 2.5
+               PFLOP/s), from HIP events recorded on the launch stream around it in
+               every timed step (the call is issued as its two phases for that)
   cpu_baseline = the float64 oracle on a bounded sample of the same workload
 """
 import argparse
@@ -25,6 +26,41 @@ if ROOT not in sys.path:
 METRIC = "verify_attn TFLOP/s and tree-verify steps/s (H=64, q_len 33/65); % MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
+
+
+KERNEL_SOURCES = ("tree_verify_mla_attn_amd/csrc/attn_bf16.hip",
+                  "tree_verify_mla_attn_amd/csrc/attn_f32.hip",
+                  "tree_verify_mla_attn_amd/csrc/common.h")
+
+
+def kernel_source_digest():
+    """sha256 over the attention kernels' sources: stored HBM counter readings are used
+    only while it still matches the digest recorded with them."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path, workload, splits):
+    """HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE readings
+    (KiB per dispatch, each scaled by the factor a plain device copy of known size gave),
+    or None when absent, for another workload, or taken on other kernel sources."""
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tj.get("workload") != workload or tj.get("num_splits") != splits \
+            or tj.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    fetch = tj["fetch_kib_per_dispatch"] * tj["fetch_copy_factor"] * 1024
+    write = tj["write_kib_per_dispatch"] * tj["write_copy_factor"] * 1024
+    return {"bytes": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write)}
 
 
 def parse():
@@ -103,9 +139,9 @@ def main():
     argv = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
             d["q_len"], inp.scale)
 
-    def step():
+    def step(mid=None):
         call(*argv, out_lat=out, out_lse=lse, num_splits=splits, max_q_len=inp.max_q_len,
-             workspace=ws, status=status)
+             workspace=ws, status=status, mid_event=mid)
 
     for _ in range(args.warmup):
         step()
@@ -115,31 +151,31 @@ def main():
         raise RuntimeError(f"device status {B.decode_status(st)}")
 
     stream = torch.cuda.current_stream(dev)
+    # Events on the launch stream: ev[i] -> mid[i] is the pre-pass (bf16 inputs),
+    # mid[i] -> ev[i + 1] the attention kernel (+ the merge when num_splits > 1).
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        step()
+        step(mid[i])
         ev[i + 1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    st = int(status.item())
+    if st:
+        raise RuntimeError(f"device status {B.decode_status(st)}")
     ms = wall * 1e3 / args.steps
-    ev_ms = sum(per_launch_ms) / len(per_launch_ms)
+    call_ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)) / args.steps
+    pre_ms = sum(ev[i].elapsed_time(mid[i]) for i in range(args.steps)) / args.steps
+    ev_ms = sum(mid[i].elapsed_time(ev[i + 1]) for i in range(args.steps)) / args.steps
 
     dtype = inp.dtype
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == inp.name and tj.get("num_splits") == splits:
-                traffic = tj.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(args.traffic_json, inp.name, splits)
 
     res = {
         "metric": METRIC,
@@ -159,12 +195,17 @@ def main():
                    "q_len": int(inp.max_q_len), "total_q": inp.total_q, "total_kv": inp.total_kv,
                    "num_splits": splits, "d_latent": 512, "d_rope": 64,
                    "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
+        "roofline": {"bound": "mfma", "kernel": "attention" + (" + merge" if splits > 1 else ""),
+                     "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic["bytes"] if traffic else None},
         "hbm": {"achieved_GBs": round(alg_bytes / (ev_ms * 1e-3) / 1e9, 1),
                 "peak_GBs": HBM_PEAK_GBS,
-                "frac": round(alg_bytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "event_ms_per_launch": round(ev_ms, 5),
+                "frac": round(alg_bytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "measured": traffic,
+                "measured_GBs": round(traffic["bytes"] / (ev_ms * 1e-3) / 1e9, 1) if traffic else None},
+        "kernel_ms": {"attention": round(ev_ms, 5), "prepass": round(pre_ms, 5),
+                      "call": round(call_ms, 5)},
     }
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)

@@ -136,6 +136,40 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
                            int64_t total_kv, int32_t dtype, int32_t num_splits,
                            void* workspace, size_t workspace_bytes, int32_t* status);
 
+/*
+ * The same call in two phases, for callers that time or schedule them apart.  Both
+ * take exactly the arguments of kdtree_verify_attn and validate them the same way.
+ *
+ *   kdtree_verify_attn_prepare   enqueues the bf16 pre-pass: it writes the request
+ *       schedule and the fp16 feature-major copies of kv_lat into `workspace`
+ *       (nothing for fp32 inputs, where it only validates).  It reads kv_lat,
+ *       prefix_len and q_len only; the other pointers must still be valid values.
+ *   kdtree_verify_attn_attend    enqueues the attention (and, with num_splits > 1,
+ *       the merge), reading the workspace that a prepare call with the same
+ *       kv_lat, prefix_len, q_len, batch, max_q_len, total_kv and dtype filled.  Until
+ *       any of those inputs change, one prepare may serve several attend calls.
+ *
+ * kdtree_verify_attn(args) == kdtree_verify_attn_prepare(args) followed by
+ * kdtree_verify_attn_attend(args) on the same stream.  Returns as kdtree_verify_attn.
+ */
+int32_t kdtree_verify_attn_prepare(const void* q_lat, const void* q_rope, const void* kv_lat,
+                                   const void* k_rope, const int32_t* prefix_len,
+                                   const int32_t* tree_parent, const int32_t* q_len,
+                                   float scale, float* out_lat, float* out_lse, void* stream,
+                                   int32_t batch, int32_t num_heads, int32_t max_q_len,
+                                   int64_t total_q, int64_t total_kv, int32_t dtype,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                   int32_t* status);
+
+int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const void* kv_lat,
+                                  const void* k_rope, const int32_t* prefix_len,
+                                  const int32_t* tree_parent, const int32_t* q_len,
+                                  float scale, float* out_lat, float* out_lse, void* stream,
+                                  int32_t batch, int32_t num_heads, int32_t max_q_len,
+                                  int64_t total_q, int64_t total_kv, int32_t dtype,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                  int32_t* status);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     names = _declared_functions()
-    assert names == ["kdtree_max_qlen", "kdtree_verify_attn", "kdtree_verify_attn_workspace_bytes"]
+    assert names == ["kdtree_max_qlen", "kdtree_verify_attn", "kdtree_verify_attn_attend",
+                     "kdtree_verify_attn_prepare", "kdtree_verify_attn_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True,
@@ -60,19 +61,23 @@ def test_workspace_bytes():
         assert B.kdtree_verify_attn_workspace_bytes(*bad) == 0
 
 
-def _call(**kw):
+def _call(entry="kdtree_verify_attn", **kw):
     args = dict(q_lat=FAKE, q_rope=FAKE, kv_lat=FAKE, k_rope=FAKE, prefix_len=FAKE,
                 tree_parent=FAKE, q_len=FAKE, scale=0.07, out_lat=FAKE, out_lse=FAKE, stream=0,
                 batch=2, num_heads=64, max_q_len=33, total_q=66, total_kv=2000, dtype=1,
                 num_splits=1, workspace=0, workspace_bytes=0, status=0)
     args.update(kw)
-    return B.kdtree_verify_attn(**args)
+    return getattr(B, entry)(**args)
 
 
+ENTRIES = list(B.ENTRY_POINTS)
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("field", ["q_lat", "q_rope", "kv_lat", "k_rope", "prefix_len",
                                    "tree_parent", "q_len", "out_lat", "out_lse"])
-def test_null_pointer_rejected(field):
-    assert _call(**{field: 0}) == -1
+def test_null_pointer_rejected(entry, field):
+    assert _call(entry, **{field: 0}) == -1
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -83,8 +88,9 @@ def test_null_pointer_rejected(field):
     (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), -5),
     (dict(scale=float("nan")), -6), (dict(scale=float("inf")), -6),
 ])
-def test_bad_arguments_rejected(kw, code):
-    assert _call(**kw) == code
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_bad_arguments_rejected(entry, kw, code):
+    assert _call(entry, **kw) == code
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -42,7 +42,13 @@ def check(name, inp, g_out, g_lse, r_out, r_lse):
     g_lse = np.asarray(g_lse, np.float64)
     e_out = np.abs(g_out - r_out)
     e_lse = np.abs(g_lse - r_lse)
-    print(f"[{name}] max|d out|={e_out.max():.3e} max|d lse|={e_lse.max():.3e}", flush=True)
+    if inp.dtype == "fp32":
+        ratio = max(e_out.max(), e_lse.max()) / FP32_ATOL
+    else:
+        ratio = max((e_out / (BF16_ATOL + BF16_RTOL * np.abs(r_out))).max(),
+                    (e_lse / (BF16_ATOL + BF16_RTOL * np.abs(r_lse))).max())
+    print(f"[{name}] max|d out|={e_out.max():.3e} max|d lse|={e_lse.max():.3e} "
+          f"worst error/bound={ratio:.3f}", flush=True)
     assert np.isfinite(g_out).all() and np.isfinite(g_lse).all()
     if inp.dtype == "fp32":
         assert e_out.max() <= FP32_ATOL, name
@@ -114,14 +120,12 @@ def test_bf16_best_first_trees_several_tiles(dev):
 
 
 # ------------------------------------------------------------------ workloads
-def test_workload1_full(dev):
-    full_check("workload1", synth.config_inputs(1), dev)
-
-
-def test_workload2_full(dev):
-    inp = synth.config_inputs(2)
-    full_check("workload2", inp, dev)
-    full_check("workload2", inp, dev, num_splits=8)
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_small_workloads_full(dev, cfg):
+    """Every element, unsplit and in the benchmark's launch configuration."""
+    inp = synth.config_inputs(cfg)
+    full_check(f"workload{cfg}", inp, dev)
+    full_check(f"workload{cfg}", inp, dev, num_splits=inp.num_splits)
 
 
 def _sample_rows(inp, rng, per_request_nodes=3, heads=(0, 63)):
@@ -237,3 +241,34 @@ def test_hip_graph_capture_replays(dev):
         g.replay()
         torch.cuda.synchronize(dev)
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_prepare_then_attend(dev, dtype):
+    """The two-phase calls give the one-call result bit for bit, and one prepare serves
+    several attend calls (also with a different split count over the same workspace)."""
+    inp = EDGE["ragged_batch5_h64"](dtype)
+    d = synth.device_tensors(inp, dev)
+    call = B.VerifyAttn()
+    dt = B.KDTREE_DTYPE_BF16 if dtype == "bf16" else B.KDTREE_DTYPE_FP32
+    ws_bytes = max(1, B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.total_kv, inp.batch,
+                                                           inp.num_heads, 4, dt))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    args = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
+            d["q_len"], inp.scale)
+    ref = {s: call(*args, num_splits=s, max_q_len=65, workspace=ws) for s in (1, 4)}
+    torch.cuda.synchronize(dev)
+    ref = {s: (o.clone(), l.clone()) for s, (o, l) in ref.items()}
+    ws.fill_(0xAB)
+    call(*args, num_splits=1, max_q_len=65, workspace=ws, phase="prepare")
+    for s in (1, 4, 1):
+        out = torch.full_like(ref[s][0], float("nan"))
+        lse = torch.full_like(ref[s][1], float("nan"))
+        call(*args, out_lat=out, out_lse=lse, num_splits=s, max_q_len=65, workspace=ws,
+             phase="attend")
+        torch.cuda.synchronize(dev)
+        assert torch.equal(out, ref[s][0]) and torch.equal(lse, ref[s][1]), f"splits={s}"
+    mid = torch.cuda.Event()
+    out, lse = call(*args, num_splits=4, max_q_len=65, workspace=ws, mid_event=mid)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(out, ref[4][0]) and torch.equal(lse, ref[4][1])

@@ -358,26 +358,47 @@ def _wrong_visibility(kind):
         elif kind == "drop_self":
             for i in range(1, t):
                 m[i, prefix_len + i] = False
+        elif kind == "descendant_mask":
+            # tail block transposed: a node sees its descendants instead of its ancestors
+            tail = m[:, prefix_len:].copy()
+            m[:, prefix_len:] = tail.T
         return m
     return vis
 
 
-@pytest.mark.parametrize("kind", ["sibling_leak", "drop_self", "rope_unscaled"])
-def test_brute_force_catches_planted_mistakes(kind, monkeypatch):
-    rng = np.random.default_rng(21)
-    par = np.array([-1, 0, 0, 1, 1, 2], np.int32)
-    inp = _tiny_inputs(22, [par], [4], heads=2)
-    bo, bl = _brute_force(inp)
-    if kind == "rope_unscaled":
-        real = O.attend_request
+_REAL_ATTEND = O.attend_request
 
-        def wrong(q_lat, q_rope, kv_lat, k_rope, mask, scale, return_probs=False):
-            # scale applied to the latent product only: rope enters unscaled
-            return real(q_lat, np.asarray(q_rope, float) / scale, kv_lat, k_rope, mask, scale,
-                        return_probs)
-        monkeypatch.setattr(O, "attend_request", wrong)
-    else:
+
+def _wrong_attend(kind):
+    def attend(q_lat, q_rope, kv_lat, k_rope, mask, scale, return_probs=False):
+        q_rope = np.asarray(q_rope, float)
+        kv_lat = np.asarray(kv_lat, float)
+        if kind == "rope_unscaled":      # scale applied to the latent product only
+            q_rope = q_rope / scale
+        elif kind == "drop_rope":        # rope dims left out of the scores
+            q_rope = np.zeros_like(q_rope)
+        elif kind == "missing_scale":
+            scale = 1.0
+        elif kind == "latent_rope_row_skew":  # latent rows one key off from rope rows
+            kv_lat = np.roll(kv_lat, 1, axis=0)
+        res = _REAL_ATTEND(q_lat, q_rope, kv_lat, k_rope, mask, scale, return_probs)
+        if kind == "log2_lse":
+            res = (res[0], res[1] / math.log(2.0)) + tuple(res[2:])
+        return res
+    return attend
+
+
+@pytest.mark.parametrize("kind", ["sibling_leak", "drop_self", "descendant_mask", "rope_unscaled",
+                                  "drop_rope", "missing_scale", "latent_rope_row_skew",
+                                  "log2_lse"])
+def test_brute_force_catches_planted_mistakes(kind, monkeypatch):
+    par = np.array([-1, 0, 0, 1, 1, 2], np.int32)
+    inp = _tiny_inputs(22, [par], [4], heads=2, scale=0.4)
+    bo, bl = _brute_force(inp)
+    if kind in ("sibling_leak", "drop_self", "descendant_mask"):
         monkeypatch.setattr(O, "visibility_mask", _wrong_visibility(kind))
+    else:
+        monkeypatch.setattr(O, "attend_request", _wrong_attend(kind))
     out, lse = _oracle(inp)
     err = max(np.abs(out - bo).max(), np.abs(lse - bl).max())
     assert err > 1e-3, f"planted mistake {kind} went unnoticed"

@@ -29,6 +29,9 @@ STATUS_BITS = {1: "bad q_len", 2: "bad prefix_len", 4: "bad tree_parent", 8: "of
 D_LATENT = 512
 D_ROPE = 64
 
+# entry points sharing the kdtree_verify_attn argument list
+ENTRY_POINTS = ("kdtree_verify_attn", "kdtree_verify_attn_prepare", "kdtree_verify_attn_attend")
+
 _lib = None
 
 
@@ -51,9 +54,11 @@ def load_library():
     lib.kdtree_max_qlen.argtypes = []
     lib.kdtree_verify_attn_workspace_bytes.restype = sz
     lib.kdtree_verify_attn_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
-    lib.kdtree_verify_attn.restype = i32
-    lib.kdtree_verify_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
-                                       i32, i32, i32, i64, i64, i32, i32, vp, sz, vp]
+    for name in ENTRY_POINTS:
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                       i32, i32, i32, i64, i64, i32, i32, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -69,14 +74,28 @@ def kdtree_verify_attn_workspace_bytes(total_q: int, total_kv: int, batch: int, 
                                                                  num_heads, num_splits, dtype))
 
 
-def kdtree_verify_attn(q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
-                       out_lat, out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv,
-                       dtype, num_splits, workspace, workspace_bytes, status) -> int:
-    """Raw call: every pointer argument is an integer device address (0 = NULL)."""
-    return int(load_library().kdtree_verify_attn(
+def _raw(name, q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale, out_lat,
+         out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv, dtype, num_splits,
+         workspace, workspace_bytes, status) -> int:
+    return int(getattr(load_library(), name)(
         q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, ctypes.c_float(scale),
         out_lat, out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv, dtype,
         num_splits, workspace, workspace_bytes, status))
+
+
+def kdtree_verify_attn(*args, **kw) -> int:
+    """Raw call: every pointer argument is an integer device address (0 = NULL)."""
+    return _raw("kdtree_verify_attn", *args, **kw)
+
+
+def kdtree_verify_attn_prepare(*args, **kw) -> int:
+    """Raw call of the pre-pass phase (same arguments as kdtree_verify_attn)."""
+    return _raw("kdtree_verify_attn_prepare", *args, **kw)
+
+
+def kdtree_verify_attn_attend(*args, **kw) -> int:
+    """Raw call of the attention phase (same arguments as kdtree_verify_attn)."""
+    return _raw("kdtree_verify_attn_attend", *args, **kw)
 
 
 # ---------------------------------------------------------------- torch convenience
@@ -111,7 +130,12 @@ class VerifyAttn:
 
     def __call__(self, q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
                  out_lat=None, out_lse=None, num_splits: int = 1,
-                 max_q_len: int = KDTREE_MAX_QLEN, workspace=None, status=None):
+                 max_q_len: int = KDTREE_MAX_QLEN, workspace=None, status=None,
+                 phase: str = "all", mid_event=None):
+        """phase: "all" (kdtree_verify_attn), "prepare" or "attend" (the two halves; an
+        "attend" call needs the `workspace` of a "prepare" call on the same inputs).
+        mid_event: with phase "all", a torch.cuda.Event recorded on the stream between
+        the two halves (the halves are then issued as two calls)."""
         import torch
         dtype = q_lat.dtype
         if dtype not in (torch.float32, torch.bfloat16):
@@ -147,15 +171,28 @@ class VerifyAttn:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_ptr = workspace.data_ptr() if (workspace is not None and need) else 0
         ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = kdtree_verify_attn(
-            q_lat.data_ptr(), q_rope.data_ptr(), kv_lat.data_ptr(), k_rope.data_ptr(),
-            prefix_len.data_ptr(), tree_parent.data_ptr(), q_len.data_ptr(), float(scale),
-            out_lat.data_ptr(), out_lse.data_ptr(), stream, batch, h, int(max_q_len), total_q,
-            total_kv, dt, int(num_splits), ws_ptr, ws_bytes,
-            status.data_ptr() if status is not None else 0)
-        if rc != 0:
-            raise RuntimeError(f"kdtree_verify_attn failed: {rc} ({ERRORS.get(rc, '?')})")
+        if phase == "attend" and need and workspace is None:
+            raise ValueError("phase 'attend' needs the workspace of a 'prepare' call")
+        torch_stream = torch.cuda.current_stream(dev)
+        args = (q_lat.data_ptr(), q_rope.data_ptr(), kv_lat.data_ptr(), k_rope.data_ptr(),
+                prefix_len.data_ptr(), tree_parent.data_ptr(), q_len.data_ptr(), float(scale),
+                out_lat.data_ptr(), out_lse.data_ptr(), torch_stream.cuda_stream, batch, h,
+                int(max_q_len), total_q, total_kv, dt, int(num_splits), ws_ptr, ws_bytes,
+                status.data_ptr() if status is not None else 0)
+        if phase == "all" and mid_event is None:
+            names = ["kdtree_verify_attn"]
+        elif phase == "all":
+            names = ["kdtree_verify_attn_prepare", "kdtree_verify_attn_attend"]
+        elif phase in ("prepare", "attend"):
+            names = ["kdtree_verify_attn_" + phase]
+        else:
+            raise ValueError(f"unknown phase {phase!r}")
+        for i, name in enumerate(names):
+            if i == 1:
+                mid_event.record(torch_stream)
+            rc = _raw(name, *args)
+            if rc != 0:
+                raise RuntimeError(f"{name} failed: {rc} ({ERRORS.get(rc, '?')})")
         return out_lat, out_lse
 
 

@@ -30,7 +30,8 @@ constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(2))) __fp16 fp16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
@@ -396,7 +397,7 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
     st.l *= st.alpha;
   }
   const float mref = st.m == -INFINITY ? 0.0f : st.m;
-  const fp16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     u32x4 packed;
@@ -404,10 +405,9 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
     for (int d = 0; d < 4; ++d) {
       const float p0 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * d] - mref);
       const float p1 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * d + 1] - mref);
-      const fp16x2 hp = __builtin_amdgcn_cvt_pkrtz(p0, p1);
-      st.l = __builtin_amdgcn_fdot2(__builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), hp),
-                                   __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), ones),
-                                   st.l, false);
+      // round to nearest even (one v_cvt_pk_f16_f32); l sums the rounded values
+      const f16x2 hp = __builtin_convertvector((f32x2){p0, p1}, f16x2);
+      st.l = __builtin_amdgcn_fdot2(hp, ones, st.l, false);
       packed[d] = __builtin_bit_cast(unsigned, hp);
     }
     pk[kk] = __builtin_bit_cast(f16x8, packed);

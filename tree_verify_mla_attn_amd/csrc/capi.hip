@@ -38,26 +38,13 @@ bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t 
   return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t kdtree_max_qlen(void) { return KDTREE_MAX_QLEN; }
-
-size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int32_t batch,
-                                          int32_t num_heads, int32_t num_splits, int32_t dtype) {
-  WorkspaceLayout w;
-  if (!workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &w)) return 0;
-  return w.total;
-}
-
-int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv_lat,
-                           const void* k_rope, const int32_t* prefix_len,
-                           const int32_t* tree_parent, const int32_t* q_len, float scale,
-                           float* out_lat, float* out_lse, void* stream, int32_t batch,
-                           int32_t num_heads, int32_t max_q_len, int64_t total_q,
-                           int64_t total_kv, int32_t dtype, int32_t num_splits,
-                           void* workspace, size_t workspace_bytes, int32_t* status) {
+// Host validation shared by the entry points; fills the launch parameters.
+int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const void* k_rope,
+              const int32_t* prefix_len, const int32_t* tree_parent, const int32_t* q_len,
+              float scale, float* out_lat, float* out_lse, int32_t batch, int32_t num_heads,
+              int32_t max_q_len, int64_t total_q, int64_t total_kv, int32_t dtype,
+              int32_t num_splits, void* workspace, size_t workspace_bytes, int32_t* status,
+              kdt::VerifyParams* pp, WorkspaceLayout* wp) {
   if (!q_lat || !q_rope || !kv_lat || !k_rope || !prefix_len || !tree_parent || !q_len ||
       !out_lat || !out_lse)
     return KDTREE_ERR_NULL;
@@ -69,12 +56,12 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
     return KDTREE_ERR_SHAPE;
   if (dtype != KDTREE_DTYPE_FP32 && dtype != KDTREE_DTYPE_BF16) return KDTREE_ERR_DTYPE;
   if (!isfinite(scale)) return KDTREE_ERR_SCALE;
-  WorkspaceLayout w;
+  WorkspaceLayout& w = *wp;
   if (!workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &w))
     return KDTREE_ERR_SPLITS;
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return KDTREE_ERR_SPLITS;
 
-  kdt::VerifyParams p;
+  kdt::VerifyParams& p = *pp;
   p.q_lat = q_lat;
   p.q_rope = q_rope;
   p.kv_lat = kv_lat;
@@ -102,23 +89,89 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
   const int bm = dtype == KDTREE_DTYPE_BF16 ? kdt::rows_per_block_bf16() : kdt::rows_per_block_f32();
   p.m_tiles = (max_q_len * num_heads + bm - 1) / bm;
   if ((int64_t)p.m_tiles * num_splits * batch > 0x7fffffff) return KDTREE_ERR_SHAPE;
+  return KDTREE_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (dtype == KDTREE_DTYPE_BF16) {
-    e = kdt::launch_vt_prepass(p, w.vt_tiles, s);
-    if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
-    e = kdt::launch_verify_bf16(p, s);
-  } else {
-    e = kdt::launch_verify_f32(p, s);
-  }
+int32_t launch_prepare(const kdt::VerifyParams& p, const WorkspaceLayout& w, int32_t dtype,
+                       hipStream_t s) {
+  if (dtype != KDTREE_DTYPE_BF16) return KDTREE_OK;
+  return kdt::launch_vt_prepass(p, w.vt_tiles, s) == hipSuccess ? KDTREE_OK : KDTREE_ERR_LAUNCH;
+}
+
+int32_t launch_attend(const kdt::VerifyParams& p, int32_t dtype, hipStream_t s) {
+  hipError_t e = dtype == KDTREE_DTYPE_BF16 ? kdt::launch_verify_bf16(p, s)
+                                            : kdt::launch_verify_f32(p, s);
   if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
-  if (num_splits > 1) {
-    e = kdt::launch_lse_merge(p.part_o, p.part_lse, out_lat, out_lse, total_q * num_heads,
-                              num_splits, s);
+  if (p.num_splits > 1) {
+    e = kdt::launch_lse_merge(p.part_o, p.part_lse, p.out_lat, p.out_lse,
+                              p.total_q * p.num_heads, p.num_splits, s);
     if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
   }
   return KDTREE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kdtree_max_qlen(void) { return KDTREE_MAX_QLEN; }
+
+size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int32_t batch,
+                                          int32_t num_heads, int32_t num_splits, int32_t dtype) {
+  WorkspaceLayout w;
+  if (!workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &w)) return 0;
+  return w.total;
+}
+
+#define KDTREE_SETUP_ARGS                                                                  \
+  q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale, out_lat, out_lse,  \
+      batch, num_heads, max_q_len, total_q, total_kv, dtype, num_splits, workspace,        \
+      workspace_bytes, status
+
+int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv_lat,
+                           const void* k_rope, const int32_t* prefix_len,
+                           const int32_t* tree_parent, const int32_t* q_len, float scale,
+                           float* out_lat, float* out_lse, void* stream, int32_t batch,
+                           int32_t num_heads, int32_t max_q_len, int64_t total_q,
+                           int64_t total_kv, int32_t dtype, int32_t num_splits,
+                           void* workspace, size_t workspace_bytes, int32_t* status) {
+  kdt::VerifyParams p;
+  WorkspaceLayout w;
+  int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
+  if (rc != KDTREE_OK) return rc;
+  rc = launch_prepare(p, w, dtype, (hipStream_t)stream);
+  if (rc != KDTREE_OK) return rc;
+  return launch_attend(p, dtype, (hipStream_t)stream);
+}
+
+int32_t kdtree_verify_attn_prepare(const void* q_lat, const void* q_rope, const void* kv_lat,
+                                   const void* k_rope, const int32_t* prefix_len,
+                                   const int32_t* tree_parent, const int32_t* q_len,
+                                   float scale, float* out_lat, float* out_lse, void* stream,
+                                   int32_t batch, int32_t num_heads, int32_t max_q_len,
+                                   int64_t total_q, int64_t total_kv, int32_t dtype,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                   int32_t* status) {
+  kdt::VerifyParams p;
+  WorkspaceLayout w;
+  int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
+  if (rc != KDTREE_OK) return rc;
+  return launch_prepare(p, w, dtype, (hipStream_t)stream);
+}
+
+int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const void* kv_lat,
+                                  const void* k_rope, const int32_t* prefix_len,
+                                  const int32_t* tree_parent, const int32_t* q_len,
+                                  float scale, float* out_lat, float* out_lse, void* stream,
+                                  int32_t batch, int32_t num_heads, int32_t max_q_len,
+                                  int64_t total_q, int64_t total_kv, int32_t dtype,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                  int32_t* status) {
+  kdt::VerifyParams p;
+  WorkspaceLayout w;
+  int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
+  if (rc != KDTREE_OK) return rc;
+  return launch_attend(p, dtype, (hipStream_t)stream);
 }
 
 }  // extern "C"

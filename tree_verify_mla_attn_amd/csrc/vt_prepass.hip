@@ -23,7 +23,8 @@ namespace kdt {
 namespace {
 
 constexpr int NTHR = 256;
-typedef __attribute__((ext_vector_type(2))) __fp16 fp16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // order[rank] = request, ranks by descending (prefix_len + q_len), ties by index
 // (malformed requests count as empty).  O(B^2 / 256) work, bounded by ORDER_MAX_BATCH.
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(NTHR) void vt_prepass_kernel(VerifyParams p) {
       const unsigned x = a[j >> 1], y = c[j >> 1];
       const float fx = __uint_as_float((j & 1) ? (x & 0xffff0000u) : (x << 16));
       const float fy = __uint_as_float((j & 1) ? (y & 0xffff0000u) : (y << 16));
-      o[d] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(fx, fy));
+      o[d] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){fx, fy}, f16x2));
     }
     const int f = fg * 8 + j;
     dst[f * 4 + (q ^ ((f >> 2) & 3))] = make_uint4(o[0], o[1], o[2], o[3]);
