@@ -465,10 +465,13 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   // ---- which (request, split, row tile) ------------------------------------------
   // Workgroup i runs on XCD i % 8.  Work comes in groups of m_tiles row tiles that share
   // one (request, split) KV range; groups are ranked by request (longest KV first, from
-  // the pre-pass) then split, and XCD x takes groups x, x+8, x+16, ...: every XCD gets an
-  // even, longest-first share, and the row tiles of a group share that XCD's L2.
+  // the pre-pass) then split, and dealt to the XCDs in snake order (ranks 0..7 to XCDs
+  // 0..7, ranks 8..15 to XCDs 7..0, ...), so every XCD gets an even, longest-first share
+  // of the work, and the row tiles of a group share that XCD's L2.
   const int slot = blockIdx.x / NUM_XCD;
-  const int grank = (int)(blockIdx.x % NUM_XCD) + NUM_XCD * (slot / p.m_tiles);
+  const int xcd = (int)(blockIdx.x % NUM_XCD);
+  const int round = slot / p.m_tiles;
+  const int grank = NUM_XCD * round + ((round & 1) ? NUM_XCD - 1 - xcd : xcd);
   if (grank >= p.batch * p.num_splits) return;
   const int mt = slot % p.m_tiles;
   const int rank = grank / p.num_splits;
