@@ -86,7 +86,7 @@ int32_t kdtree_max_qlen(void);
 /* Workspace bytes kdtree_verify_attn needs (0 = none).  Returns 0 for invalid sizes.
  * Regions (each rounded up to 256 bytes):
  *   bf16 inputs: the request schedule (batch int32) and fp16 copies of the latent rows,
- *     feature-major in 32-key tiles, both written by a pre-pass of the same call:
+ *     key-major in 32-key tiles, both written by a pre-pass of the same call:
  *     batch * 4 and (total_kv / 32 + batch + 1) * 32 KB bytes;
  *   num_splits > 1: split partial outputs num_splits * total_q * num_heads * 512 * 4
  *     bytes and their log-sum-exps num_splits * total_q * num_heads * 4 bytes. */
@@ -97,9 +97,10 @@ size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int
  * Tree-verify MLA-absorb attention (see the top of this file).
  *
  *   q_lat, q_rope, kv_lat, k_rope   device inputs, dtype `dtype` (fp32 / bf16).
- *       bf16 contract: values must be finite with |x| < 65504 in kv_lat (the
- *       softmax-weighted sum of latent rows runs as an fp16 contraction, which
- *       represents every such bf16 value exactly above 2^-24).
+ *       bf16 contract: values must be finite with |x| < 65504 in q_lat and kv_lat
+ *       (the latent contractions run as fp16 MFMAs with fp32 accumulation; bf16 ->
+ *       fp16 is exact for 2^-17 <= |x| < 65504, smaller magnitudes round with an
+ *       absolute error <= 2^-25).
  *   prefix_len, tree_parent, q_len  device int32 arrays (layout above).
  *   scale        softmax scale applied to q . k (finite; e.g. 1/sqrt(192)).
  *   out_lat      device fp32 [total_q, H, 512];  out_lse device fp32 [total_q, H].
@@ -141,7 +142,7 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
  * take exactly the arguments of kdtree_verify_attn and validate them the same way.
  *
  *   kdtree_verify_attn_prepare   enqueues the bf16 pre-pass: it writes the request
- *       schedule and the fp16 feature-major copies of kv_lat into `workspace`
+ *       schedule and the fp16 key-major copies of kv_lat into `workspace`
  *       (nothing for fp32 inputs, where it only validates).  It reads kv_lat,
  *       prefix_len and q_len only; the other pointers must still be valid values.
  *   kdtree_verify_attn_attend    enqueues the attention (and, with num_splits > 1,

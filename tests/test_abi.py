@@ -47,7 +47,7 @@ def test_workspace_bytes():
         return -(-x // 256) * 256
     # fp32, one split: nothing
     assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 0) == 0
-    # bf16, one split: the fp16 V^T tiles only
+    # bf16, one split: the request order and the fp16 latent tiles only
     assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 1) == up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768)
     # bf16, 16 splits: tiles + partial outputs + partial lse
     tq, tkv, b, h, s = 260, 131332, 4, 64, 16

@@ -9,15 +9,18 @@
 // Work decomposition (one workgroup = 4 waves = 128 query rows of one request and one
 // KV split).  Rows are packed node-major, head-minor, so all heads of a node share its
 // ancestor mask and all 128 rows share every KV tile.  Each wave owns 32 rows:
-//   * Q fragment (32 rows x 576, bf16) lives in VGPRs for the whole KV loop;
-//   * S^T = K Q^T per 32-key tile: bf16 MFMA 32x32x16, so each lane holds one query
-//     row and the softmax row reductions are in-register plus one lane swap;
+//   * Q fragment (32 rows x 576: latent part converted to fp16, rope part bf16) lives in
+//     VGPRs for the whole KV loop;
+//   * S^T = K Q^T per 32-key tile: fp16 MFMA 32x32x16 over the latent dims, bf16 over
+//     the rope dims, so each lane holds one query row and the softmax row reductions are
+//     in-register plus one lane swap;
 //   * online softmax in the log2 domain with a lazy rescale (the running max is only
 //     raised when a tile beats it by more than 2^8);
 //   * O^T += V^T P^T: fp16 MFMA 32x32x16 with P in fp16 (bf16 P is too coarse for a
-//     2e-3 relative bound) against an fp16, feature-major copy of the latent tile.
-// KV tiles (32 keys x 576 bf16) and the matching fp16 V^T tiles (converted once per
-// call by the pre-pass) arrive by 16-byte global->LDS DMA into double-buffered LDS.
+//     2e-3 relative bound); V^T operands are read from the same fp16 latent tile as K,
+//     through the transposing LDS load.
+// The fp16 latent tiles (converted once per call by the pre-pass) and the bf16 rope rows
+// arrive by 16-byte global->LDS DMA into a three-stage LDS ring.
 #include "common.h"
 
 namespace kdt {
@@ -30,279 +33,254 @@ constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 #define LDS_AS __attribute__((address_space(3)))
 
-// LDS tiles, two stages, one buffer.  Per stage (u32x4 = 16 B units):
-//   K latent [32 keys][64 chunks + 1 pad]: chunk c of key k at slot k*65 + c (the pad
-//            staggers rows across banks and keeps every k-step a constant offset);
-//   K rope   [32 keys][8 chunks]:  chunk c of key k at slot k*8 + (c ^ rswz(k));
-//   V^T fp16 [512 features][4 chunks of 8 keys]: chunk q of feature f at
-//            vt_slot(f, q) = f*4 + (q ^ ((f >> 2) & 3)) -- the pre-pass's tile image; the
-//            swizzle keeps the PV reads (32 consecutive features) bank-conflict free.
-constexpr int KLAT_ROW = 65;
-constexpr int KLAT_U4 = BN * KLAT_ROW, KROPE_U4 = BN * 8, VT_U4 = DL * 4;
+// LDS tiles, three stages.  Per stage (u32x4 = 16 B units):
+//   K16    [32 keys][64 chunks + 4 pad] fp16 latent rows, 8 features per chunk: chunk c
+//          of key k at slot k*68 + (c ^ ksw(k)), ksw(k) = (k >> 2) & 3.  The score reads
+//          (16 consecutive keys, one chunk each) and the transposing value reads (4
+//          consecutive keys x 4 chunks) are both bank-conflict free, and both address
+//          streams stay affine (two base registers each);
+//   K rope [32 keys][8 chunks] bf16: chunk c of key k at slot k*8 + (c ^ rswz(k)).
+// Tile j serves the scores (loop trip j-1) and the values (trip j) while tile j+2 is in
+// flight: three stages.
+constexpr int K16_ROW = 68;
+constexpr int K16_U4 = BN * K16_ROW, KROPE_U4 = BN * 8;
+constexpr int K16_STEP16 = 16 * K16_ROW * 16;  // bytes between key rows r and r + 16
 // Separate objects per stage: the compiler's wait-count insertion can then tell that a
-// DMA into one stage does not alias LDS reads of the other, and does not stall the
+// DMA into one stage does not alias LDS reads of another, and does not stall the
 // compute of tile j on the in-flight copy of tile j+2.
-__shared__ __attribute__((aligned(1024))) u32x4 sKlat0[KLAT_U4];
-__shared__ __attribute__((aligned(1024))) u32x4 sKlat1[KLAT_U4];
-__shared__ __attribute__((aligned(1024))) u32x4 sKrope0[KROPE_U4];
-__shared__ __attribute__((aligned(1024))) u32x4 sKrope1[KROPE_U4];
-__shared__ __attribute__((aligned(1024))) u32x4 sVt0[VT_U4];
-__shared__ __attribute__((aligned(1024))) u32x4 sVt1[VT_U4];
+__shared__ __attribute__((aligned(1024))) u32x4 sK16a[K16_U4];
+__shared__ __attribute__((aligned(1024))) u32x4 sK16b[K16_U4];
+__shared__ __attribute__((aligned(1024))) u32x4 sK16c[K16_U4];
+__shared__ __attribute__((aligned(1024))) u32x4 sKropeA[KROPE_U4];
+__shared__ __attribute__((aligned(1024))) u32x4 sKropeB[KROPE_U4];
+__shared__ __attribute__((aligned(1024))) u32x4 sKropeC[KROPE_U4];
 __shared__ int32_t sParent[MAX_QLEN];
 __shared__ int64_t sRed[3 * 4];
 __shared__ int32_t sFlag;
 
 __device__ __forceinline__ int rswz(int k) { return (k ^ (k >> 3)) & 7; }
-__device__ __forceinline__ int vt_slot(int f, int q) { return f * 4 + (q ^ ((f >> 2) & 3)); }
+__device__ __forceinline__ int ksw(int k) { return (k >> 2) & 3; }
 
-template <int STAGE> __device__ __forceinline__ u32x4* klat() { return STAGE ? sKlat1 : sKlat0; }
-template <int STAGE> __device__ __forceinline__ u32x4* krope() { return STAGE ? sKrope1 : sKrope0; }
-template <int STAGE> __device__ __forceinline__ u32x4* vt() { return STAGE ? sVt1 : sVt0; }
-
-__device__ __forceinline__ void dma16(const char* uniform_base, unsigned lane_off, u32x4* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)(uniform_base + lane_off), (LDS_AS void*)lds_base, 16,
-                                   0, 0);
+template <int S> __device__ __forceinline__ u32x4* k16() {
+  return S == 0 ? sK16a : (S == 1 ? sK16b : sK16c);
+}
+template <int S> __device__ __forceinline__ u32x4* krope() {
+  return S == 0 ? sKropeA : (S == 1 ? sKropeB : sKropeC);
 }
 
-// Issue the DMA of keys [key0, key0+32) of this request (rows clamped to key_last) into
-// a stage.  Wave w moves latent rows 8w..8w+7 (one contiguous 1 KB row per instruction)
-// and rope rows 8w..8w+7 (one instruction).  Row pointers are wave-uniform; lanes only
-// add a 32-bit offset.
-template <int STAGE>
-__device__ __forceinline__ void issue_tile(const char* kv_lat_req, const char* k_rope_req,
-                                           int key0, int key_last, int wave, int lane) {
-  u32x4* kl = klat<STAGE>();
-  u32x4* kr = krope<STAGE>();
+// 16-byte global -> LDS copy per lane (64 lanes fill 1 KB at lds_base) through a buffer
+// descriptor on the wave-uniform base (lane offsets below 2^31).  The buffer form, unlike
+// global_load_lds, is counted by the compiler's wait insertion as a vector-memory
+// operation only, so LDS reads issued while copies are in flight keep exact lgkmcnt
+// waits instead of draining every outstanding LDS read.
+__device__ __forceinline__ void dma16(const char* uniform_base, unsigned lane_off, u32x4* lds_base) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_base, (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)lds_base, 16, (int)lane_off, 0, 0,
+                                           0);
+}
+
+// One fp16 latent row (1 KB, already in its LDS image) per DMA.
+template <int S>
+__device__ __forceinline__ void dma_k16_row(const char* tile, int row, unsigned lane_off) {
+  dma16(tile + row * 1024, lane_off, k16<S>() + row * K16_ROW);
+}
+
+// Rope rows 8w..8w+7 of keys [key0, key0+32) (clamped to key_last), one instruction per
+// wave: lane l moves chunk (l & 7) of row 8w + (l >> 3) into its swizzled slot.
+template <int S>
+__device__ __forceinline__ void dma_rope(const char* k_rope_req, int key0, int key_last, int wave,
+                                         int lane) {
+  const int key = wave * 8 + (lane >> 3);
+  const int k = min(key0 + key, key_last);
+  dma16(k_rope_req, (unsigned)k * (DR * 2) + (unsigned)((lane & 7) ^ rswz(key)) * 16u,
+        krope<S>() + wave * 64);
+}
+
+// Issue the DMA of tile `tile` (keys [key0, key0+32)) into stage S.  Wave w moves fp16
+// latent rows 8w..8w+7 and rope rows 8w..8w+7.
+template <int S>
+__device__ __forceinline__ void issue_tile(const char* tile, const char* k_rope_req, int key0,
+                                           int key_last, int wave, int lane) {
   // Re-materialise the lane id here so the per-lane offsets are recomputed per tile
-  // instead of being hoisted out of the KV loop as eight long-lived registers.
+  // instead of being hoisted out of the KV loop as long-lived registers.
   asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = wave * 8 + i;
-    const int k = __builtin_amdgcn_readfirstlane(min(key0 + key, key_last));
-    dma16(kv_lat_req + (int64_t)k * (DL * 2), (unsigned)lane * 16u, kl + key * KLAT_ROW);
-  }
-  {
-    const int key = wave * 8 + (lane >> 3);
-    const int k = min(key0 + key, key_last);
-    const unsigned off = (unsigned)k * (DR * 2) + (unsigned)((lane & 7) ^ rswz(key)) * 16u;
-    dma16(k_rope_req, off, kr + wave * 64);
-  }
+  for (int i = 0; i < 8; ++i) dma_k16_row<S>(tile, wave * 8 + i, (unsigned)lane * 16u);
+  dma_rope<S>(k_rope_req, key0, key_last, wave, lane);
 }
 
-// DMA of the pre-converted V^T tile `tile` into a stage (wave w moves 1 KB blocks
-// 8w..8w+7 of the 32 KB tile image).
-template <int STAGE>
-__device__ __forceinline__ void issue_vt(const char* vt_req, int tile, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = wave * 8 + i;
-    dma16(vt_req + (int64_t)tile * VT_TILE_BYTES + blk * 1024, (unsigned)lane * 16u,
-          vt<STAGE>() + blk * 64);
+// Score fragment ks of the tile in stage S for this lane (key = lane & 31, half h):
+// latent k-steps 0..31 read chunk 2ks + h of the key's fp16 row, rope k-steps 32..35
+// read the bf16 rope row.
+struct ScoreFrags {
+  int be, bo, rrow, rkey;
+  __device__ __forceinline__ ScoreFrags(int lane) {
+    const int key = lane & 31, h = lane >> 5, sw = ksw(key);
+    // chunk 2ks + h lands in slot 4 (ks >> 1) + ((2 (ks & 1) + h) ^ sw) of the row
+    be = key * K16_ROW + (h ^ sw);
+    bo = key * K16_ROW + ((2 + h) ^ sw);
+    rrow = key * 8;
+    rkey = key;
   }
+  template <int S>
+  __device__ __forceinline__ u32x4 get(int ks, int h) const {
+    if (ks < 32) return k16<S>()[((ks & 1) ? bo : be) + 4 * (ks >> 1)];
+    const int c = 2 * ks + h - 64;
+    return krope<S>()[rrow + (c ^ rswz(rkey))];
+  }
+};
+
+__device__ __forceinline__ f32x16 mfma_qk(int ks, const u32x4& a, const u32x4& q, const f32x16& s) {
+  if (ks < 32)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, q), s, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, q), s, 0, 0, 0);
 }
 
-// S^T (32 keys x 32 rows of this wave) for the tile in a stage.  K fragments are read
+// S^T (32 keys x 32 rows of this wave) for the tile in stage S.  K fragments are read
 // four MFMAs ahead of use.
-template <int STAGE>
+template <int S>
 __device__ __forceinline__ f32x16 qk_tile(const u32x4 (&qf)[36], int lane) {
-  const u32x4* kl = klat<STAGE>();
-  const u32x4* kr = krope<STAGE>();
-  const int key = lane & 31, h = lane >> 5;
-  auto frag = [&](int ks) -> u32x4 {
-    const int c = 2 * ks + h;
-    return ks < 32 ? kl[key * KLAT_ROW + c] : kr[key * 8 + ((c - 64) ^ rswz(key))];
-  };
+  const ScoreFrags fr(lane);
+  const int h = lane >> 5;
   u32x4 a[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = frag(i);
+  for (int i = 0; i < 4; ++i) a[i] = fr.get<S>(i, h);
   f32x16 s = {};
 #pragma unroll
   for (int ks = 0; ks < 36; ++ks) {
-    if (ks + 4 < 36) a[(ks + 4) & 7] = frag(ks + 4);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks & 7]),
-                                                __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
+    if (ks + 4 < 36) a[(ks + 4) & 7] = fr.get<S>(ks + 4, h);
+    s = mfma_qk(ks, a[ks & 7], qf[ks], s);
+    __builtin_amdgcn_sched_barrier(0);  // keep each read four MFMAs ahead of its use
   }
   return s;
 }
 
-// Scores of the next tile fused with the copies that must be in flight meanwhile: the
-// K tile j+2 into stage SC and the V^T tile j+1 into stage SN.  One 1 KB DMA is
-// spliced after every two score MFMAs, so the copy engine's queue drains in the shadow
-// of the matrix pipe instead of stalling the wave in one burst.
-template <int SC, int SN>
-__device__ __forceinline__ f32x16 qk_dma(const u32x4 (&qf)[36], int lane, const char* kv_lat_req,
-                                         const char* k_rope_req, const char* vt_req, int k_key0,
-                                         int key_last, int vt_tile, int wave) {
-  const u32x4* kl = klat<SN>();
-  const u32x4* kr = krope<SN>();
-  const int key = lane & 31, h = lane >> 5;
-  auto frag = [&](int ks) -> u32x4 {
-    const int c = 2 * ks + h;
-    return ks < 32 ? kl[key * KLAT_ROW + c] : kr[key * 8 + ((c - 64) ^ rswz(key))];
-  };
+// Scores of the next tile (stage SQ) fused with the copy of the tile after it into stage
+// SD: nine DMAs (eight fp16 latent rows, one rope instruction), one after every four
+// score MFMAs, so the copy engine's queue drains in the shadow of the matrix pipe.
+template <int SQ, int SD>
+__device__ __forceinline__ f32x16 qk_dma(const u32x4 (&qf)[36], int lane, const char* dma_tile,
+                                         const char* k_rope_req, int k_key0, int key_last,
+                                         int wave) {
+  const ScoreFrags fr(lane);
+  const int h = lane >> 5;
   u32x4 a[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = frag(i);
+  for (int i = 0; i < 4; ++i) a[i] = fr.get<SQ>(i, h);
   f32x16 s = {};
   int dl = lane;
   asm volatile("" : "+v"(dl));  // per-tile lane offsets, not hoisted out of the KV loop
-  auto dma = [&](int n) {
-    if (n < 8) {          // K latent row wave*8 + n
-      const int kk = wave * 8 + n;
-      const int k = __builtin_amdgcn_readfirstlane(min(k_key0 + kk, key_last));
-      dma16(kv_lat_req + (int64_t)k * (DL * 2), (unsigned)dl * 16u, klat<SC>() + kk * KLAT_ROW);
-    } else if (n == 8) {  // K rope rows wave*8 .. +7
-      const int kk = wave * 8 + (dl >> 3);
-      const int k = min(k_key0 + kk, key_last);
-      dma16(k_rope_req, (unsigned)k * (DR * 2) + (unsigned)((dl & 7) ^ rswz(kk)) * 16u,
-            krope<SC>() + wave * 64);
-    } else {              // V^T tile: 1 KB blocks wave*8 + (n - 9)
-      const int blk = wave * 8 + (n - 9);
-      dma16(vt_req + (int64_t)vt_tile * VT_TILE_BYTES + blk * 1024, (unsigned)dl * 16u,
-            vt<SN>() + blk * 64);
-    }
-  };
+  const int key0s = __builtin_amdgcn_readfirstlane(k_key0);
+  const int lasts = __builtin_amdgcn_readfirstlane(key_last);
 #pragma unroll
   for (int ks = 0; ks < 36; ++ks) {
-    if (ks + 4 < 36) a[(ks + 4) & 7] = frag(ks + 4);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks & 7]),
-                                                __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
-    if ((ks & 1) && (ks >> 1) < 17) dma(ks >> 1);
+    if (ks + 4 < 36) a[(ks + 4) & 7] = fr.get<SQ>(ks + 4, h);
+    s = mfma_qk(ks, a[ks & 7], qf[ks], s);
+    if ((ks & 3) == 3) {
+      const int n = ks >> 2;  // 0..8
+      if (n < 8) dma_k16_row<SD>(dma_tile, wave * 8 + n, (unsigned)dl * 16u);
+      else dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each read four MFMAs ahead of its use
   }
   return s;
 }
 
-// O^T += V^T P^T for one 32-key tile: 16 feature blocks x 2 key steps of fp16 MFMA
-// 32x32x16.  Written as one asm block so that the 16 output accumulators stay in the
-// AGPR file (256 registers) across the KV loop while Q, S and P use VGPRs.  V^T
-// fragments stream through eight rotating VGPR buffers, each LDS read issued four
-// MFMAs ahead of its use; LDS reads return in order, so lgkmcnt(n) proves the oldest
-// of this block's reads has landed.  The leading s_nop covers VALU writes of P / O
-// (softmax, rescale) feeding the first MFMA; the trailing ones cover MFMA results
-// read by VALU code after the block.
-template <int STAGE>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const f16x8 (&pk)[2], int lane) {
-  const int fl = lane & 31, h = lane >> 5;
-  // feature 32*fb + fl lives at byte vt_slot(fl, .)*16 + fb*2048
-  const unsigned base = (unsigned)(size_t)(LDS_AS void*)vt<STAGE>();
-  const unsigned v0 = base + (unsigned)(vt_slot(fl, 0 + h) * 16);
-  const unsigned v1 = base + (unsigned)(vt_slot(fl, 2 + h) * 16);
-  u32x4 t0, t1, t2, t3, t4, t5, t6, t7;
-  asm volatile(
-      "s_nop 4\n"
-      "ds_read_b128 %[a0], %[v0] offset:0\n"
-      "ds_read_b128 %[a1], %[v1] offset:0\n"
-      "ds_read_b128 %[a2], %[v0] offset:2048\n"
-      "ds_read_b128 %[a3], %[v1] offset:2048\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o0], %[a0], %[p0], %[o0]\n"
-      "ds_read_b128 %[a4], %[v0] offset:4096\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o0], %[a1], %[p1], %[o0]\n"
-      "ds_read_b128 %[a5], %[v1] offset:4096\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o1], %[a2], %[p0], %[o1]\n"
-      "ds_read_b128 %[a6], %[v0] offset:6144\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o1], %[a3], %[p1], %[o1]\n"
-      "ds_read_b128 %[a7], %[v1] offset:6144\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o2], %[a4], %[p0], %[o2]\n"
-      "ds_read_b128 %[a0], %[v0] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o2], %[a5], %[p1], %[o2]\n"
-      "ds_read_b128 %[a1], %[v1] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o3], %[a6], %[p0], %[o3]\n"
-      "ds_read_b128 %[a2], %[v0] offset:10240\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o3], %[a7], %[p1], %[o3]\n"
-      "ds_read_b128 %[a3], %[v1] offset:10240\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o4], %[a0], %[p0], %[o4]\n"
-      "ds_read_b128 %[a4], %[v0] offset:12288\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o4], %[a1], %[p1], %[o4]\n"
-      "ds_read_b128 %[a5], %[v1] offset:12288\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o5], %[a2], %[p0], %[o5]\n"
-      "ds_read_b128 %[a6], %[v0] offset:14336\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o5], %[a3], %[p1], %[o5]\n"
-      "ds_read_b128 %[a7], %[v1] offset:14336\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o6], %[a4], %[p0], %[o6]\n"
-      "ds_read_b128 %[a0], %[v0] offset:16384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o6], %[a5], %[p1], %[o6]\n"
-      "ds_read_b128 %[a1], %[v1] offset:16384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o7], %[a6], %[p0], %[o7]\n"
-      "ds_read_b128 %[a2], %[v0] offset:18432\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o7], %[a7], %[p1], %[o7]\n"
-      "ds_read_b128 %[a3], %[v1] offset:18432\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o8], %[a0], %[p0], %[o8]\n"
-      "ds_read_b128 %[a4], %[v0] offset:20480\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o8], %[a1], %[p1], %[o8]\n"
-      "ds_read_b128 %[a5], %[v1] offset:20480\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o9], %[a2], %[p0], %[o9]\n"
-      "ds_read_b128 %[a6], %[v0] offset:22528\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o9], %[a3], %[p1], %[o9]\n"
-      "ds_read_b128 %[a7], %[v1] offset:22528\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o10], %[a4], %[p0], %[o10]\n"
-      "ds_read_b128 %[a0], %[v0] offset:24576\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o10], %[a5], %[p1], %[o10]\n"
-      "ds_read_b128 %[a1], %[v1] offset:24576\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o11], %[a6], %[p0], %[o11]\n"
-      "ds_read_b128 %[a2], %[v0] offset:26624\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o11], %[a7], %[p1], %[o11]\n"
-      "ds_read_b128 %[a3], %[v1] offset:26624\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o12], %[a0], %[p0], %[o12]\n"
-      "ds_read_b128 %[a4], %[v0] offset:28672\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o12], %[a1], %[p1], %[o12]\n"
-      "ds_read_b128 %[a5], %[v1] offset:28672\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o13], %[a2], %[p0], %[o13]\n"
-      "ds_read_b128 %[a6], %[v0] offset:30720\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o13], %[a3], %[p1], %[o13]\n"
-      "ds_read_b128 %[a7], %[v1] offset:30720\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %[o14], %[a4], %[p0], %[o14]\n"
-      "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_f16 %[o14], %[a5], %[p1], %[o14]\n"
-      "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_f16 %[o15], %[a6], %[p0], %[o15]\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_f16 %[o15], %[a7], %[p1], %[o15]\n"
-      "s_nop 7\n s_nop 7\n s_nop 3\n"
-      : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
-        [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
-        [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]),
-        [o14] "+a"(o[14]), [o15] "+a"(o[15]), [a0] "=&v"(t0), [a1] "=&v"(t1), [a2] "=&v"(t2),
-        [a3] "=&v"(t3), [a4] "=&v"(t4), [a5] "=&v"(t5), [a6] "=&v"(t6), [a7] "=&v"(t7)
-      : [v0] "v"(v0), [v1] "v"(v1), [p0] "v"(pk[0]), [p1] "v"(pk[1])
-      : "memory");
+// o[FB] += a * p (fp16 MFMA 32x32x16).  Every accumulator is an operand of every such
+// statement, which pins all 16 to fixed AGPRs for the whole loop; naming only o[FB]
+// lets the allocator route them through one AGPR tuple with copies.
+#define KDT_PV_OPERANDS                                                                    \
+  : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),   \
+    [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),   \
+    [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]),            \
+    [o14] "+a"(o[14]), [o15] "+a"(o[15])                                                   \
+  : [a] "v"(a), [p] "v"(p)
+#define KDT_PV_CASE(N)                                                                      \
+  if constexpr (FB == N)                                                                    \
+  asm volatile("v_mfma_f32_32x32x16_f16 %[o" #N "], %[a], %[p], %[o" #N "]" KDT_PV_OPERANDS)
+template <int FB>
+__device__ __forceinline__ void mfma_pv(f32x16 (&o)[16], const f16x8& a, const f16x8& p) {
+  KDT_PV_CASE(0); KDT_PV_CASE(1); KDT_PV_CASE(2); KDT_PV_CASE(3);
+  KDT_PV_CASE(4); KDT_PV_CASE(5); KDT_PV_CASE(6); KDT_PV_CASE(7);
+  KDT_PV_CASE(8); KDT_PV_CASE(9); KDT_PV_CASE(10); KDT_PV_CASE(11);
+  KDT_PV_CASE(12); KDT_PV_CASE(13); KDT_PV_CASE(14); KDT_PV_CASE(15);
 }
+#undef KDT_PV_CASE
+#undef KDT_PV_OPERANDS
+
+// V^T operand of feature block fb, key step ks: eight fp16 of feature 32fb + (lane & 31)
+// at the k-slots 8h..8h+7 of the P operand (keys 16ks + 4h + {0..3, 8..11}), as two
+// transposing 8-byte loads of four consecutive key rows each.
+struct ValueFrags {
+  const LDS_AS char* base;
+  unsigned off0, off1;
+  __device__ __forceinline__ ValueFrags(const u32x4* tile, int lane) {
+    base = (const LDS_AS char*)(LDS_AS void*)tile;
+    const int g = (lane >> 4) & 1, r = (lane >> 2) & 3, q = lane & 3, h = lane >> 5;
+    // lane 4r + q of a 16-lane group reads 4 features (8 B) of key row 4h + 8j + r; the
+    // row swizzle ksw = h + 2j there, chunk 4fb + 2g + (q >> 1)
+    off0 = (unsigned)((4 * h + r) * K16_ROW * 16 + 16 * ((2 * g + (q >> 1)) ^ h) + 8 * (q & 1));
+    off1 = (unsigned)((4 * h + 8 + r) * K16_ROW * 16 + 16 * ((2 * g + (q >> 1)) ^ (h + 2)) +
+                      8 * (q & 1));
+  }
+  template <int FB, int KS>
+  __device__ __forceinline__ f16x8 get() const {
+    constexpr unsigned step = (unsigned)(KS * K16_STEP16 + FB * 64);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base + off0 + step));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base + off1 + step));
+    const f16x4 l4 = __builtin_bit_cast(f16x4, lo), h4 = __builtin_bit_cast(f16x4, hi);
+    return f16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+  }
+};
+
+// Feature blocks FB..15 of one PV tile: the V^T operands of block FB+2 are read, then the
+// two MFMAs of block FB issue, fenced so the order holds.
+template <int FB>
+__device__ __forceinline__ void pv_block(f32x16 (&o)[16], const f16x8 (&pk)[2], f16x8 (&a)[6],
+                                         const ValueFrags& vf) {
+  if constexpr (FB < 16) {
+    if constexpr (FB + 2 < 16) {
+      a[((FB + 2) % 3) * 2] = vf.get<FB + 2, 0>();
+      a[((FB + 2) % 3) * 2 + 1] = vf.get<FB + 2, 1>();
+    }
+    mfma_pv<FB>(o, a[(FB % 3) * 2], pk[0]);
+    mfma_pv<FB>(o, a[(FB % 3) * 2 + 1], pk[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_block<FB + 1>(o, pk, a, vf);
+  }
+}
+
+// O^T += V^T P^T for the tile in stage S: 16 feature blocks x 2 key steps of fp16 MFMA
+// 32x32x16 with the 16 output accumulators pinned in AGPRs.  P passes through the s_nop
+// statement: its VALU producers (softmax) must complete before the wait states, which
+// then cover the hazard of a VALU write feeding an MFMA operand (the compiler does not
+// pad for MFMAs inside asm statements).
+template <int S>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const f16x8 (&pk)[2], int lane) {
+  const ValueFrags vf(k16<S>(), lane);
+  f16x8 a[6];
+  f16x8 pp[2] = {pk[0], pk[1]};
+  asm volatile("s_nop 4" : "+v"(pp[0]), "+v"(pp[1]));
+  a[0] = vf.get<0, 0>();
+  a[1] = vf.get<0, 1>();
+  a[2] = vf.get<1, 0>();
+  a[3] = vf.get<1, 1>();
+  pv_block<0>(o, pp, a, vf);
+}
+
+// Wait states between the last PV MFMA and VALU reads of the accumulators.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n s_nop 7\n s_nop 3"); }
 
 // max / sum of x over the lane pair (l, l ^ 32) that shares a query row, without an
 // LDS round trip: v_permlane32_swap exchanges the upper half of one copy with the lower
@@ -406,7 +384,7 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
       const float p0 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * d] - mref);
       const float p1 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * d + 1] - mref);
       // round to nearest even (one v_cvt_pk_f16_f32); l sums the rounded values
-      const f16x2 hp = __builtin_convertvector((f32x2){p0, p1}, f16x2);
+      const f16x2 hp = {(_Float16)p0, (_Float16)p1};
       st.l = __builtin_amdgcn_fdot2(hp, ones, st.l, false);
       packed[d] = __builtin_bit_cast(unsigned, hp);
     }
@@ -414,21 +392,20 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
   }
 }
 
-// One pipelined trip of the KV loop for tile j held in stage STAGE = j & 1: softmax and
-// PV of tile j, scores and V^T conversion of tile j+1, DMA of tile j+2 into the other
-// stage's K buffer.  One barrier per tile.
+// One pipelined trip of the KV loop for tile j, held in stage ST = j % 3: softmax and PV
+// of tile j, scores of tile j+1 (stage (j+1) % 3), DMA of tile j+2 into the stage tile
+// j-1 used.  One barrier per tile.
 struct TileLoop {
-  const char* kv_lat;
   const char* k_rope;
-  const char* vt;  // this split's first V^T tile
-  int k_begin;     // first key of tile 0 (32-aligned)
-  int k_first;     // first key of the split's range (>= k_begin)
+  const char* k16;  // this split's first fp16 latent tile
+  int k_begin;      // first key of tile 0 (32-aligned)
+  int k_first;      // first key of the split's range (>= k_begin)
   int k_end, key_last, n_tiles, mask_from, prefix, node;
   uint64_t anc;
   float c;
   int tid, wave, lane;
 
-  template <int STAGE>
+  template <int ST>
   __device__ __forceinline__ void iteration(int j, f32x16& s_cur, f32x16 (&o)[16], RowState& st,
                                             const u32x4 (&qf)[36]) const {
     const int key0 = k_begin + j * BN;
@@ -438,17 +415,19 @@ struct TileLoop {
     f16x8 pk[2];
     softmax_tile(s_cur, pk, st, c, masked, vis, lane);
     if (__builtin_expect(st.rescale, 0)) {
+      mfma_drain();
 #pragma unroll
       for (int fb = 0; fb < 16; ++fb) o[fb] = scale_acc(o[fb], st.alpha);
     }
     const bool more = j + 1 < n_tiles;
     if (more) {
-      // Past the last tile the DMA is clamped to the last key: a harmless refill of a
-      // buffer nobody reads any more.
-      s_cur = qk_dma<STAGE, STAGE ^ 1>(qf, lane, kv_lat, k_rope, vt, key0 + 2 * BN, key_last,
-                                       j + 1, wave);
+      // Past the last tile the copy repeats the last one: a harmless refill of a stage
+      // nobody reads any more.
+      const int jd = min(j + 2, n_tiles - 1);
+      s_cur = qk_dma<(ST + 1) % 3, (ST + 2) % 3>(qf, lane, k16 + (int64_t)jd * TILE_BYTES, k_rope,
+                                                 key0 + 2 * BN, key_last, wave);
     }
-    pv_tile<STAGE>(o, pk, lane);
+    pv_tile<ST>(o, pk, lane);
     if (more) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -489,7 +468,7 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
     bad |= pl < 0 ? ST_BAD_PREFIX : 0;
     qoff += t;
     kvoff += (int64_t)pl + t;
-    tbase += ((int64_t)pl + t + VT_TILE_KEYS - 1) / VT_TILE_KEYS;
+    tbase += ((int64_t)pl + t + TILE_KEYS - 1) / TILE_KEYS;
   }
   for (int off = 32; off > 0; off >>= 1) {
     qoff += __shfl_xor(qoff, off);
@@ -583,13 +562,24 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
       const int c = 2 * ks + h;
       qf[ks] = ks < 32 ? *(const u32x4*)(ql + c * 16) : *(const u32x4*)(qr + (c - 64) * 16);
     }
+    // latent part to fp16 (the scores contract it against the fp16 latent tiles); exact
+    // for 2^-17 <= |x| < 65504 like the tiles themselves
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const unsigned x = qf[ks][d];
+        const f16x2 hp = {(_Float16)__uint_as_float(x << 16),
+                          (_Float16)__uint_as_float(x & 0xffff0000u)};
+        qf[ks][d] = __builtin_bit_cast(unsigned, hp);
+      }
+    }
   }
 
-  const char* kv_lat = (const char*)p.kv_lat + kvoff * (DL * 2);  // this request's rows
-  const char* k_rope = (const char*)p.k_rope + kvoff * (DR * 2);
-  // Tiles are 32-aligned in the request's key stream (the V^T tiles are); a split whose
-  // range starts mid-tile (only the last split, when the prefix is short) masks the keys
-  // before its range.
+  const char* k_rope = (const char*)p.k_rope + kvoff * (DR * 2);  // this request's rows
+  // Tiles are 32-aligned in the request's key stream (the fp16 latent tiles are); a split
+  // whose range starts mid-tile (only the last split, when the prefix is short) masks the
+  // keys before its range.
   const int k_first = k_begin;
   k_begin &= ~(BN - 1);
   const int key_last = k_end - 1;
@@ -602,30 +592,31 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   for (int fb = 0; fb < 16; ++fb) o[fb] = f32x16{};
   RowState st{-INFINITY, 0.0f, 1.0f, false};
 
-  // Pipeline: iteration j runs the softmax and PV of tile j while the scores of tile
-  // j+1 are computed and its V^T converted; the DMA of tile j+2 is in flight.  One
-  // barrier per tile.  Stage j&1 holds K(j) / V^T(j).
-  if (tbase + (P + T + BN - 1) / BN > p.vt_tiles) {  // cannot happen for valid offsets
+  // Pipeline: trip j runs the softmax and PV of tile j (stage j % 3) while the scores of
+  // tile j+1 are computed; the DMA of tile j+2 is in flight.  One barrier per tile.
+  if (tbase + (P + T + BN - 1) / BN > p.k16_tiles) {  // cannot happen for valid offsets
     if (tid == 0 && p.status) atomicOr(p.status, ST_OVERFLOW);
     return;
   }
-  const char* vt_split = (const char*)p.vt + (tbase + k_begin / BN) * VT_TILE_BYTES;
-  issue_tile<0>(kv_lat, k_rope, k_begin, key_last, wave, lane);
-  issue_vt<0>(vt_split, 0, wave, lane);
+  const char* k16_split = (const char*)p.k16 + (tbase + k_begin / BN) * TILE_BYTES;
+  issue_tile<0>(k16_split, k_rope, k_begin, key_last, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (n_tiles > 1) issue_tile<1>(kv_lat, k_rope, k_begin + BN, key_last, wave, lane);
+  if (n_tiles > 1) issue_tile<1>(k16_split + TILE_BYTES, k_rope, k_begin + BN, key_last, wave, lane);
   f32x16 s_cur = qk_tile<0>(qf, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  TileLoop tl{kv_lat, k_rope, vt_split, k_begin, k_first, k_end, key_last, n_tiles, mask_from,
+  TileLoop tl{k_rope, k16_split, k_begin, k_first, k_end, key_last, n_tiles, mask_from,
               P, node, anc, c, tid, wave, lane};
-  for (int j = 0; j < n_tiles; j += 2) {
+  for (int j = 0; j < n_tiles; j += 3) {
     tl.iteration<0>(j, s_cur, o, st, qf);
     if (j + 1 >= n_tiles) break;
     tl.iteration<1>(j + 1, s_cur, o, st, qf);
+    if (j + 2 >= n_tiles) break;
+    tl.iteration<2>(j + 2, s_cur, o, st, qf);
   }
+  mfma_drain();
 
   // ---- finalize -------------------------------------------------------------------
   const float l_tot = pair_sum(st.l);

@@ -14,27 +14,27 @@ constexpr int32_t kMaxSplits = 256;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t order_bytes, vt_bytes, part_o_bytes, part_lse_bytes, total;
-  int64_t vt_tiles;
+  size_t order_bytes, k16_bytes, part_o_bytes, part_lse_bytes, total;
+  int64_t k16_tiles;
 };
 
-// Workspace: [request order + fp16 V^T tiles (bf16 inputs)] [split partial outputs]
-// [split lse], each
-// region 256-byte aligned.  V^T tiles: one 32 KB tile per 32 keys of every request,
-// bounded by total_kv / 32 + batch (each request adds at most one partial tile).
+// Workspace: [request order + fp16 latent tiles (bf16 inputs)] [split partial outputs]
+// [split lse], each region 256-byte aligned.  Latent tiles: one 32 KB tile per 32 keys
+// of every request, bounded by total_kv / 32 + batch (each request adds at most one
+// partial tile).
 bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t num_heads,
                       int32_t num_splits, int32_t dtype, WorkspaceLayout* w) {
   if (total_q < 1 || total_kv < 1 || batch < 1 || num_heads < 1 || num_splits < 1 ||
       num_splits > kMaxSplits || (dtype != KDTREE_DTYPE_FP32 && dtype != KDTREE_DTYPE_BF16))
     return false;
   if (total_q > ((int64_t)1 << 40) || total_kv > ((int64_t)1 << 40)) return false;
-  w->vt_tiles = dtype == KDTREE_DTYPE_BF16 ? total_kv / kdt::VT_TILE_KEYS + batch + 1 : 0;
+  w->k16_tiles = dtype == KDTREE_DTYPE_BF16 ? total_kv / kdt::TILE_KEYS + batch + 1 : 0;
   w->order_bytes = dtype == KDTREE_DTYPE_BF16 ? round_up((size_t)batch * 4, 256) : 0;
-  w->vt_bytes = round_up((size_t)w->vt_tiles * (size_t)kdt::VT_TILE_BYTES, 256);
+  w->k16_bytes = round_up((size_t)w->k16_tiles * (size_t)kdt::TILE_BYTES, 256);
   const size_t rows = (size_t)total_q * (size_t)num_heads;
   w->part_o_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * kdt::DL * sizeof(float), 256) : 0;
   w->part_lse_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * sizeof(float), 256) : 0;
-  w->total = w->order_bytes + w->vt_bytes + w->part_o_bytes + w->part_lse_bytes;
+  w->total = w->order_bytes + w->k16_bytes + w->part_o_bytes + w->part_lse_bytes;
   return true;
 }
 
@@ -73,11 +73,11 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
   p.out_lse = out_lse;
   char* ws = (char*)workspace;
   p.order = w.order_bytes ? (int32_t*)ws : nullptr;
-  p.vt = w.vt_bytes ? ws + w.order_bytes : nullptr;
-  p.vt_tiles = w.vt_tiles;
-  p.part_o = num_splits > 1 ? (float*)(ws + w.order_bytes + w.vt_bytes) : nullptr;
+  p.k16 = w.k16_bytes ? ws + w.order_bytes : nullptr;
+  p.k16_tiles = w.k16_tiles;
+  p.part_o = num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes) : nullptr;
   p.part_lse =
-      num_splits > 1 ? (float*)(ws + w.order_bytes + w.vt_bytes + w.part_o_bytes) : nullptr;
+      num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes + w.part_o_bytes) : nullptr;
   p.status = status;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.batch = batch;
@@ -95,7 +95,7 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
 int32_t launch_prepare(const kdt::VerifyParams& p, const WorkspaceLayout& w, int32_t dtype,
                        hipStream_t s) {
   if (dtype != KDTREE_DTYPE_BF16) return KDTREE_OK;
-  return kdt::launch_vt_prepass(p, w.vt_tiles, s) == hipSuccess ? KDTREE_OK : KDTREE_ERR_LAUNCH;
+  return kdt::launch_prepass(p, w.k16_tiles, s) == hipSuccess ? KDTREE_OK : KDTREE_ERR_LAUNCH;
 }
 
 int32_t launch_attend(const kdt::VerifyParams& p, int32_t dtype, hipStream_t s) {

@@ -11,8 +11,8 @@ constexpr int DR = 64;           // rope dims (scores only)
 constexpr int DK = DL + DR;      // score contraction depth
 constexpr int MAX_QLEN = 65;     // draft budget 64 + root
 constexpr int MAX_REQUEST_KEYS = 1 << 24;  // prefix_len + q_len of one request
-constexpr int VT_TILE_KEYS = 32;           // keys per pre-converted V^T tile
-constexpr int64_t VT_TILE_BYTES = DL * VT_TILE_KEYS * 2;
+constexpr int TILE_KEYS = 32;              // keys per pre-converted fp16 latent tile
+constexpr int64_t TILE_BYTES = DL * TILE_KEYS * 2;
 constexpr int ORDER_MAX_BATCH = 4096;      // larger batches keep the request order as given
 constexpr int NUM_XCD = 8;                 // MI355X: workgroup i runs on XCD i % 8
 constexpr float LN2 = 0.69314718055994530942f;
@@ -34,18 +34,18 @@ struct VerifyParams {
   float* part_o;     // [num_splits, total_q*H, 512] (num_splits > 1)
   float* part_lse;   // [num_splits, total_q*H]
   int32_t* status;   // nullable
-  void* vt;          // bf16 path: fp16 V^T tiles (32 keys each) written by the pre-pass
+  void* k16;         // bf16 path: fp16 latent tiles (32 keys each) written by the pre-pass
   int32_t* order;    // bf16 path: requests by descending KV length (written by the pre-pass)
   float scale_log2;  // scale * log2(e)
   int32_t batch, num_heads, max_q_len, num_splits, m_tiles;
   int64_t total_q, total_kv;
-  int64_t vt_tiles;  // capacity of `vt` in tiles
+  int64_t k16_tiles; // capacity of `k16` in tiles
 };
 
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_verify_f32(const VerifyParams& p, hipStream_t stream);
-hipError_t launch_vt_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStream_t stream);
+hipError_t launch_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, float* out_lat,
                             float* out_lse, int64_t rows, int32_t num_splits, hipStream_t stream);
 int rows_per_block_bf16();

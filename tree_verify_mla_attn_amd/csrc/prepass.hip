@@ -1,21 +1,24 @@
-// V^T pre-pass for the bf16 path: the latent rows of every request's KV stream,
-// converted once to fp16 and laid out feature-major in 32-key tiles, exactly as the
-// attention kernel's PV contraction reads them from LDS.
+// Pre-pass of the bf16 path: the latent rows of every request's KV stream, converted once
+// per call to fp16 and laid out in 32-key tiles exactly as the attention kernel keeps
+// them in LDS, where each tile serves both contractions: the scores read its rows (8
+// latent features per lane) and the softmax-weighted sum reads it through the transposing
+// LDS load (4 keys per lane).
 //
-// Why: the softmax-weighted sum of latent rows runs as an fp16 MFMA (P must be fp16:
-// bf16 P is too coarse for a 2e-3 relative bound), so V must be fp16 too, and the MFMA
-// operand wants 8 consecutive keys of one feature.  Converting here, once per call,
-// keeps the conversion and its LDS traffic out of the attention loop, where each KV
-// tile is consumed by every row tile of its request.
+// Why fp16: the weighted sum of latent rows runs as an fp16 MFMA (P must be fp16: bf16 P
+// is too coarse for a 2e-3 relative bound), so V must be fp16; the scores then use the
+// same copy.  bf16 -> fp16 is exact for 2^-17 <= |x| < 65504 (fp16 normals carry 11
+// significant bits, its subnormals reach every bf16 value down to 2^-17); smaller
+// magnitudes round with an absolute error <= 2^-25.  Converting here, once per call,
+// keeps the conversion out of the attention loop, where each tile is consumed by every
+// row tile of its request.
 //
 // Workgroup 0 also ranks the requests by KV length (longest first; ties by index) into
 // p.order, which the attention kernel uses to hand out work longest-first.
 //
 // Tile t of request b covers keys [32t, 32t+32) of that request's stream (prefix, then
-// tail); keys past the end repeat the last key (their probabilities are zero).  Tile
-// layout (u32x4 = 8 fp16 keys of one feature): feature f, key chunk q at slot
-// f*4 + (q ^ ((f >> 2) & 3)); chunk q holds keys {b..b+3, b+8..b+11} with
-// b = 16(q/2) + 4(q%2), in the k-slot order of the PV MFMA.  Tiles of request b start at
+// tail); keys past the end repeat the last key (their probabilities are zero, their
+// values stay finite).  Tile image: row r (key 32t + r) = 1 KB = 64 chunks of 8 fp16
+// features; slot s of row r holds chunk s ^ ((r >> 2) & 3).  Tiles of request b start at
 // tile index sum_{b' < b} ceil((P_b' + T_b') / 32).
 #include "common.h"
 
@@ -24,7 +27,6 @@ namespace {
 
 constexpr int NTHR = 256;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // order[rank] = request, ranks by descending (prefix_len + q_len), ties by index
 // (malformed requests count as empty).  O(B^2 / 256) work, bounded by ORDER_MAX_BATCH.
@@ -52,7 +54,7 @@ __device__ void rank_requests(const VerifyParams& p) {
   }
 }
 
-__global__ __launch_bounds__(NTHR) void vt_prepass_kernel(VerifyParams p) {
+__global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
   __shared__ int64_t s_kvoff, s_tbase;
   __shared__ int s_b, s_flag;
   const int tid = threadIdx.x;
@@ -107,38 +109,38 @@ __global__ __launch_bounds__(NTHR) void vt_prepass_kernel(VerifyParams p) {
   const int n_keys = p.prefix_len[b] + p.q_len[b];
   const int key0 = (int)(g - s_tbase) * 32;
 
-  const int q = tid & 3, fg = tid >> 2;
-  const int kb = 16 * (q >> 1) + 4 * (q & 1);
-  const uint4* src = (const uint4*)p.kv_lat;  // bf16 rows of 64 x 16 B
+  // wave w converts rows 8w..8w+7, one contiguous 1 KB row per instruction: lane l reads
+  // chunk l (8 bf16) and writes it, as 8 fp16, to slot l ^ ((row >> 2) & 3)
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint4* src = (const uint4*)p.kv_lat;  // bf16 rows: 64 x 16 B
+  uint4* dst = (uint4*)p.k16 + g * (DL * 2 / 16 * 32);
   uint4 w[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int k = min(key0 + kb + (e >> 2) * 8 + (e & 3), n_keys - 1);
-    w[e] = src[(kvoff + k) * 64 + fg];
+    const int k = min(key0 + wave * 8 + e, n_keys - 1);
+    w[e] = src[(kvoff + k) * 64 + lane];
   }
-  uint4* dst = (uint4*)p.vt + g * (DL * 4);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int e = 0; e < 8; ++e) {
+    const int row = wave * 8 + e;
     unsigned o[4];
+    const unsigned* x = (const unsigned*)&w[e];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const unsigned* a = (const unsigned*)&w[2 * d];
-      const unsigned* c = (const unsigned*)&w[2 * d + 1];
-      const unsigned x = a[j >> 1], y = c[j >> 1];
-      const float fx = __uint_as_float((j & 1) ? (x & 0xffff0000u) : (x << 16));
-      const float fy = __uint_as_float((j & 1) ? (y & 0xffff0000u) : (y << 16));
-      o[d] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){fx, fy}, f16x2));
+      // bf16 pair -> fp32 pair (exact) -> fp16 pair, round to nearest even
+      const f16x2 hp = {(_Float16)__uint_as_float(x[d] << 16),
+                        (_Float16)__uint_as_float(x[d] & 0xffff0000u)};
+      o[d] = __builtin_bit_cast(unsigned, hp);
     }
-    const int f = fg * 8 + j;
-    dst[f * 4 + (q ^ ((f >> 2) & 3))] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[row * 64 + (lane ^ ((row >> 2) & 3))] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
 }  // namespace
 
-hipError_t launch_vt_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStream_t stream) {
+hipError_t launch_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStream_t stream) {
   if (n_tiles_bound <= 0 || n_tiles_bound > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(vt_prepass_kernel, dim3((unsigned)n_tiles_bound), dim3(NTHR), 0, stream, p);
+  hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)n_tiles_bound), dim3(NTHR), 0, stream, p);
   return hipGetLastError();
 }
 
