@@ -306,3 +306,50 @@ def device_tensors(inp: VerifyInputs, device="cuda"):
     return dict(q_lat=t(inp.q_lat), q_rope=t(inp.q_rope), kv_lat=t(inp.kv_lat),
                 k_rope=t(inp.k_rope), prefix_len=ti(inp.prefix_len),
                 tree_parent=ti(inp.tree_parent), q_len=ti(inp.q_len))
+
+
+# ------------------------------------------------------ draft tables and target tokens
+VOCAB = 163840
+
+
+def draft_tables(rng: np.random.Generator, batch: int, top_k, depth: int = MAX_DEPTH,
+                 vocab: int = VOCAB):
+    """Drafter outputs for the tree builder: per request and draft position, K
+    log-probabilities (float32, sorted descending) and K distinct token ids.
+
+    Returns (logp [batch, depth, K] float32, token_ids [batch, depth, K] int32,
+    root_token [batch] int32).  ``top_k`` may be one value or one per request (then
+    the tables use the largest K and the other requests' extra columns are -inf)."""
+    ks = [top_k] * batch if np.isscalar(top_k) else list(top_k)
+    kmax = max(ks)
+    logp = np.full((batch, depth, kmax), -np.inf, np.float32)
+    ids = np.zeros((batch, depth, kmax), np.int32)
+    for b in range(batch):
+        logp[b, :, :ks[b]] = logprob_table(rng, ks[b], depth).astype(np.float32)
+        for d in range(depth):
+            ids[b, d] = rng.choice(vocab, size=kmax, replace=False)
+    root = rng.integers(0, vocab, size=batch).astype(np.int32)
+    return logp, ids, root
+
+
+def children_lists(parent: np.ndarray) -> List[List[int]]:
+    """Children of every node of one tree, in index order."""
+    kids: List[List[int]] = [[] for _ in range(len(parent))]
+    for i in range(1, len(parent)):
+        kids[int(parent[i])].append(i)
+    return kids
+
+
+def target_next_tokens(rng: np.random.Generator, parent: np.ndarray, token: np.ndarray,
+                       p_follow: float, width: int, vocab: int = VOCAB) -> np.ndarray:
+    """Synthetic target-model greedy next tokens for one tree: at every node, with
+    probability p_follow the token of one of its children (chosen uniformly), else a
+    random token.  Returns [width] int32 (entries past the tree are -1)."""
+    out = np.full(width, -1, np.int32)
+    kids = children_lists(parent)
+    for i in range(len(parent)):
+        if kids[i] and rng.random() < p_follow:
+            out[i] = token[kids[i][int(rng.integers(0, len(kids[i])))]]
+        else:
+            out[i] = int(rng.integers(0, vocab))
+    return out
