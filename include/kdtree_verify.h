@@ -171,6 +171,115 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
                                   int32_t* status);
 
+/* ------------------------------------------------------------------------------------
+ * The steps on either side of verify attention in one greedy DDTree step.
+ * ------------------------------------------------------------------------------------ */
+
+/* Limits of kdtree_build_ddtree. */
+#define KDTREE_MAX_BUDGET 64     /* drafted nodes per tree: q_len <= 65 */
+#define KDTREE_MAX_DEPTH 64      /* draft positions per request */
+#define KDTREE_MAX_TABLE 4096    /* depth * top_k of one request's candidate table */
+
+/*
+ * Best-first draft-tree builder on the device, one wavefront per request ("The Milestone
+ * Commit: Cementing Phase 1 ...", section "The Context", item 1: the builder runs on the
+ * GPU in place of a per-request host heap; "Strategic Pivots in CUDA Kernel Engineering
+ * ...", sections "The Message" and "Why This Message Was Written": trees from the
+ * drafter's top-k log-probabilities and token ids, budgets up to 64, exact agreement with
+ * the host heap including its tie-breaks and float32 accumulation).
+ *
+ *   logp        device fp32 [batch, depth, top_k]: for draft position d (0-based row) the
+ *               drafter's top_k log-probabilities, sorted descending; -inf marks an absent
+ *               candidate (rows shorter than top_k).  No NaN.
+ *   token_ids   device int32 [batch, depth, top_k]: the token of each candidate.
+ *   root_token  device int32 [batch]: token of node 0 (the last verified token).
+ *   batch >= 1; 1 <= depth <= 64; 1 <= top_k <= 4095; depth * top_k <= 4096;
+ *   0 <= budget <= 64 (drafted nodes besides the root).
+ *
+ * The tree: node 0 is the root with score 0.  A node at depth d >= 1 taking rank r
+ * carries token_ids[b][d-1][r] and the score parent + logp[b][d-1][r], added in float32.
+ * Nodes are popped from a frontier by highest score, ties to the earliest pushed; popping
+ * (d, r) under parent p pushes (d, r+1) under p and (d+1, 0) under the new node; node
+ * index = pop order.  The tree stops at budget drafted nodes or an empty frontier, so
+ * q_len[b] = drafted nodes + 1 <= budget + 1, and parent[i] < i (the layout
+ * kdtree_verify_attn takes, once packed).
+ *
+ * Outputs, device int32 [batch, budget + 1] (row b of request b; entries at and past
+ * q_len[b] are -1):
+ *   tree_parent   parent node (-1 for the root);
+ *   tree_token    token (root: root_token[b]);
+ *   tree_depth    depth (root: 0);
+ *   first_child   lowest-index child, or -1;
+ *   next_sibling  next-higher-index node with the same parent, or -1;
+ *   tree_score    optional (NULL = not written) fp32 [batch, budget + 1]: the node
+ *                 scores, -inf past q_len[b].
+ *   q_len         device int32 [batch].
+ * Ownership and stream rules as for kdtree_verify_attn; no workspace.  Returns
+ * KDTREE_OK after enqueueing, KDTREE_ERR_NULL for a missing required pointer,
+ * KDTREE_ERR_SHAPE for sizes outside the limits, KDTREE_ERR_LAUNCH on a launch failure.
+ */
+int32_t kdtree_build_ddtree(const float* logp, const int32_t* token_ids,
+                            const int32_t* root_token, int32_t batch, int32_t depth,
+                            int32_t top_k, int32_t budget, int32_t* q_len, int32_t* tree_parent,
+                            int32_t* tree_token, int32_t* tree_depth, int32_t* first_child,
+                            int32_t* next_sibling, float* tree_score, void* stream);
+
+/*
+ * Pack the builder's padded rows into the packed node-order layout kdtree_verify_attn
+ * reads, on the device (the verify step consumes the builder's output without a host
+ * round trip: "The Capstone Commit ...", section "The Message Itself", the on-device
+ * build -> accept composition and the bridge that takes the builder's device output).
+ *
+ *   q_len        device int32 [batch]: nodes per tree (clamped to [0, width]).
+ *   tree_parent  device int32 [batch, width]; tree_token the same or NULL.
+ *   total_q      rows of the packed outputs (>= sum of q_len; a request that would end
+ *                past total_q is not written).
+ *   packed_parent device int32 [total_q]: request b's nodes at rows
+ *                [q_offsets[b], q_offsets[b] + q_len[b]) (local indices, as given).
+ *   packed_token device int32 [total_q] or NULL (then tree_token may be NULL).
+ *   q_offsets    device int64 [batch + 1] or NULL: exclusive prefix sums of the clamped
+ *                q_len, q_offsets[batch] = their total.
+ * Returns KDTREE_OK, KDTREE_ERR_NULL, KDTREE_ERR_SHAPE (batch < 1, width outside
+ * [1, 2^20], total_q < 1) or KDTREE_ERR_LAUNCH.
+ */
+int32_t kdtree_pack_tree(const int32_t* q_len, const int32_t* tree_parent,
+                         const int32_t* tree_token, int32_t batch, int32_t width, int64_t total_q,
+                         int32_t* packed_parent, int32_t* packed_token, int64_t* q_offsets,
+                         void* stream);
+
+/*
+ * Greedy follow-verified-tree accept, one thread per request ("The Milestone Commit
+ * ...", section "The Context", item 3: a walk over the verified tree's next-token and
+ * next-sibling pointers).
+ *
+ *   tree_token, first_child, next_sibling   device int32 [batch, max_nodes], as written
+ *               by kdtree_build_ddtree (max_nodes = budget + 1).
+ *   q_len       device int32 [batch]: nodes of each tree (clamped to [1, max_nodes]).
+ *   target_next device int32 [batch, max_nodes]: the target model's greedy next token
+ *               after node i (the argmax of its logits at query row i).
+ *   max_accept  columns of the outputs (>= 1); at most max_accept - 1 draft nodes are
+ *               accepted, so that the bonus token always fits.
+ *
+ * From the root, the walk moves to the first child (in sibling order) whose token equals
+ * target_next at the current node, and stops at the first node with no such child,
+ * emitting target_next there as the bonus token.  Pointers that leave [1, q_len) or do
+ * not increase the node index end the walk as "no such child".
+ *
+ * Outputs:
+ *   accept_len     device int32 [batch]: accepted draft nodes + 1 (the bonus token).
+ *   accept_tokens  device int32 [batch, max_accept]: the accepted tokens, then the bonus
+ *                  token, then -1.
+ *   accept_nodes   device int32 [batch, max_accept]: node index of each accepted token,
+ *                  -1 for the bonus token and the padding.
+ * Returns as kdtree_build_ddtree (KDTREE_ERR_SHAPE: batch, max_nodes or max_accept < 1
+ * or > 2^20).
+ */
+int32_t kdtree_tree_accept(const int32_t* tree_token, const int32_t* first_child,
+                           const int32_t* next_sibling, const int32_t* q_len,
+                           const int32_t* target_next, int32_t batch, int32_t max_nodes,
+                           int32_t max_accept, int32_t* accept_len, int32_t* accept_tokens,
+                           int32_t* accept_nodes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,9 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     names = _declared_functions()
-    assert names == ["kdtree_max_qlen", "kdtree_verify_attn", "kdtree_verify_attn_attend",
+    assert names == ["kdtree_build_ddtree", "kdtree_max_qlen", "kdtree_pack_tree",
+                     "kdtree_tree_accept",
+                     "kdtree_verify_attn", "kdtree_verify_attn_attend",
                      "kdtree_verify_attn_prepare", "kdtree_verify_attn_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -116,3 +118,76 @@ def test_choose_num_splits():
     assert B.choose_num_splits(1, 64, 33, 2081) >= 2
     assert B.choose_num_splits(64, 64, 33, 5000) == 1
     assert B.choose_num_splits(4, 64, 65, 32833) >= 2
+
+
+# ---------------------------------------------------------------- builder and accept
+def _build(**kw):
+    args = dict(logp=FAKE, token_ids=FAKE, root_token=FAKE, batch=2, depth=15, top_k=8,
+                budget=64, q_len=FAKE, tree_parent=FAKE, tree_token=FAKE, tree_depth=FAKE,
+                first_child=FAKE, next_sibling=FAKE, tree_score=0, stream=0)
+    args.update(kw)
+    return B.kdtree_build_ddtree(**args)
+
+
+@pytest.mark.parametrize("field", ["logp", "token_ids", "root_token", "q_len", "tree_parent",
+                                   "tree_token", "tree_depth", "first_child", "next_sibling"])
+def test_build_null_pointer_rejected(field):
+    assert _build(**{field: 0}) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(depth=0), dict(depth=65), dict(top_k=0),
+                                dict(top_k=4096, depth=1), dict(depth=64, top_k=65),
+                                dict(budget=-1), dict(budget=65)])
+def test_build_bad_shape_rejected(kw):
+    assert _build(**kw) == -2
+
+
+def test_build_limits_match_header():
+    text = open(HEADER).read()
+    for name in ("KDTREE_MAX_BUDGET", "KDTREE_MAX_DEPTH", "KDTREE_MAX_TABLE"):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name)
+    src = open(os.path.join(ROOT, "tree_verify_mla_attn_amd", "csrc", "common.h")).read()
+    for name, c in (("KDTREE_MAX_BUDGET", "MAX_DDTREE_BUDGET"), ("KDTREE_MAX_DEPTH", "MAX_DDTREE_DEPTH"),
+                    ("KDTREE_MAX_TABLE", "MAX_DDTREE_TABLE")):
+        m = re.search(rf"constexpr int {c} = (\d+);", src)
+        assert m and int(m.group(1)) == getattr(B, name)
+
+
+def _accept(**kw):
+    args = dict(tree_token=FAKE, first_child=FAKE, next_sibling=FAKE, q_len=FAKE,
+                target_next=FAKE, batch=2, max_nodes=65, max_accept=16, accept_len=FAKE,
+                accept_tokens=FAKE, accept_nodes=FAKE, stream=0)
+    args.update(kw)
+    return B.kdtree_tree_accept(**args)
+
+
+@pytest.mark.parametrize("field", ["tree_token", "first_child", "next_sibling", "q_len",
+                                   "target_next", "accept_len", "accept_tokens", "accept_nodes"])
+def test_accept_null_pointer_rejected(field):
+    assert _accept(**{field: 0}) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(max_nodes=0), dict(max_accept=0),
+                                dict(max_nodes=(1 << 20) + 1), dict(max_accept=(1 << 20) + 1)])
+def test_accept_bad_shape_rejected(kw):
+    assert _accept(**kw) == -2
+
+
+def _pack(**kw):
+    args = dict(q_len=FAKE, tree_parent=FAKE, tree_token=FAKE, batch=2, width=33, total_q=66,
+                packed_parent=FAKE, packed_token=FAKE, q_offsets=0, stream=0)
+    args.update(kw)
+    return B.kdtree_pack_tree(**args)
+
+
+@pytest.mark.parametrize("kw", [dict(q_len=0), dict(tree_parent=0), dict(packed_parent=0),
+                                dict(tree_token=0)])
+def test_pack_null_pointer_rejected(kw):
+    assert _pack(**kw) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(width=0), dict(width=(1 << 20) + 1),
+                                dict(total_q=0)])
+def test_pack_bad_shape_rejected(kw):
+    assert _pack(**kw) == -2

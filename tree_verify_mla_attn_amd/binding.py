@@ -20,6 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_LIB = os.path.join(HERE, "libkdtree_verify.so")
 
 KDTREE_MAX_QLEN = 65
+KDTREE_MAX_BUDGET = 64
+KDTREE_MAX_DEPTH = 64
+KDTREE_MAX_TABLE = 4096
 KDTREE_DTYPE_FP32 = 0
 KDTREE_DTYPE_BF16 = 1
 ERRORS = {0: "OK", -1: "null pointer", -2: "bad shape", -3: "bad max_q_len", -4: "bad dtype",
@@ -59,6 +62,13 @@ def load_library():
         fn.restype = i32
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                        i32, i32, i32, i64, i64, i32, i32, vp, sz, vp]
+    lib.kdtree_build_ddtree.restype = i32
+    lib.kdtree_build_ddtree.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                        vp, vp]
+    lib.kdtree_pack_tree.restype = i32
+    lib.kdtree_pack_tree.argtypes = [vp, vp, vp, i32, i32, i64, vp, vp, vp, vp]
+    lib.kdtree_tree_accept.restype = i32
+    lib.kdtree_tree_accept.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -98,7 +108,121 @@ def kdtree_verify_attn_attend(*args, **kw) -> int:
     return _raw("kdtree_verify_attn_attend", *args, **kw)
 
 
+def kdtree_build_ddtree(logp, token_ids, root_token, batch, depth, top_k, budget, q_len,
+                        tree_parent, tree_token, tree_depth, first_child, next_sibling,
+                        tree_score, stream) -> int:
+    """Raw call of the draft-tree builder (pointers as integer device addresses)."""
+    return int(load_library().kdtree_build_ddtree(
+        logp, token_ids, root_token, batch, depth, top_k, budget, q_len, tree_parent,
+        tree_token, tree_depth, first_child, next_sibling, tree_score, stream))
+
+
+def kdtree_pack_tree(q_len, tree_parent, tree_token, batch, width, total_q, packed_parent,
+                     packed_token, q_offsets, stream) -> int:
+    """Raw call of the padded -> packed tree conversion (pointers as device addresses)."""
+    return int(load_library().kdtree_pack_tree(q_len, tree_parent, tree_token, batch, width,
+                                               total_q, packed_parent, packed_token, q_offsets,
+                                               stream))
+
+
+def kdtree_tree_accept(tree_token, first_child, next_sibling, q_len, target_next, batch,
+                       max_nodes, max_accept, accept_len, accept_tokens, accept_nodes,
+                       stream) -> int:
+    """Raw call of the greedy tree accept (pointers as integer device addresses)."""
+    return int(load_library().kdtree_tree_accept(
+        tree_token, first_child, next_sibling, q_len, target_next, batch, max_nodes,
+        max_accept, accept_len, accept_tokens, accept_nodes, stream))
+
+
 # ---------------------------------------------------------------- torch convenience
+def _check_dev(t, name, dtype, shape):
+    import torch  # noqa: F401
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def build_ddtree(logp, token_ids, root_token, budget: int, with_score: bool = True):
+    """Draft trees of a batch on the device.
+
+    logp fp32 [B, D, K] (rows sorted descending, -inf = absent), token_ids int32 [B, D, K],
+    root_token int32 [B].  Returns a dict of [B, budget + 1] tensors (parent, token, depth,
+    first_child, next_sibling, and score if ``with_score``; -1 / -inf past q_len) plus
+    q_len [B], all on the inputs' device, written on the current stream."""
+    import torch
+    if logp.dim() != 3:
+        raise ValueError("logp must be [batch, depth, top_k]")
+    b, d, k = (int(x) for x in logp.shape)
+    _check_dev(logp, "logp", torch.float32, (b, d, k))
+    _check_dev(token_ids, "token_ids", torch.int32, (b, d, k))
+    _check_dev(root_token, "root_token", torch.int32, (b,))
+    dev, w = logp.device, int(budget) + 1
+    out = {n: torch.empty((b, w), dtype=torch.int32, device=dev)
+           for n in ("parent", "token", "depth", "first_child", "next_sibling")}
+    out["q_len"] = torch.empty((b,), dtype=torch.int32, device=dev)
+    if with_score:
+        out["score"] = torch.empty((b, w), dtype=torch.float32, device=dev)
+    rc = kdtree_build_ddtree(
+        logp.data_ptr(), token_ids.data_ptr(), root_token.data_ptr(), b, d, k, int(budget),
+        out["q_len"].data_ptr(), out["parent"].data_ptr(), out["token"].data_ptr(),
+        out["depth"].data_ptr(), out["first_child"].data_ptr(), out["next_sibling"].data_ptr(),
+        out["score"].data_ptr() if with_score else 0, torch.cuda.current_stream(dev).cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"kdtree_build_ddtree failed: {rc} ({ERRORS.get(rc, '?')})")
+    return out
+
+
+def pack_tree(q_len, tree_parent, tree_token=None, total_q: Optional[int] = None):
+    """Padded [B, W] tree rows -> packed rows on the device.  Returns (packed_parent
+    [total_q], packed_token [total_q] or None, q_offsets int64 [B + 1]); total_q defaults
+    to B * W (the capacity: rows past q_offsets[B] are left unwritten)."""
+    import torch
+    if tree_parent.dim() != 2:
+        raise ValueError("tree_parent must be [batch, width]")
+    b, w = (int(x) for x in tree_parent.shape)
+    _check_dev(tree_parent, "tree_parent", torch.int32, (b, w))
+    _check_dev(q_len, "q_len", torch.int32, (b,))
+    if tree_token is not None:
+        _check_dev(tree_token, "tree_token", torch.int32, (b, w))
+    dev = tree_parent.device
+    total_q = b * w if total_q is None else int(total_q)
+    packed_parent = torch.empty((total_q,), dtype=torch.int32, device=dev)
+    packed_token = None if tree_token is None else torch.empty((total_q,), dtype=torch.int32,
+                                                               device=dev)
+    q_offsets = torch.empty((b + 1,), dtype=torch.int64, device=dev)
+    rc = kdtree_pack_tree(q_len.data_ptr(), tree_parent.data_ptr(),
+                          0 if tree_token is None else tree_token.data_ptr(), b, w, total_q,
+                          packed_parent.data_ptr(),
+                          0 if packed_token is None else packed_token.data_ptr(),
+                          q_offsets.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"kdtree_pack_tree failed: {rc} ({ERRORS.get(rc, '?')})")
+    return packed_parent, packed_token, q_offsets
+
+
+def tree_accept(tree_token, first_child, next_sibling, q_len, target_next, max_accept: int):
+    """Greedy accept of a batch on the device.  The tree arrays and target_next are int32
+    [B, N]; q_len int32 [B].  Returns (accept_len [B], accept_tokens [B, max_accept],
+    accept_nodes [B, max_accept]), written on the current stream."""
+    import torch
+    if tree_token.dim() != 2:
+        raise ValueError("tree_token must be [batch, max_nodes]")
+    b, n = (int(x) for x in tree_token.shape)
+    for t, name in ((tree_token, "tree_token"), (first_child, "first_child"),
+                    (next_sibling, "next_sibling"), (target_next, "target_next")):
+        _check_dev(t, name, torch.int32, (b, n))
+    _check_dev(q_len, "q_len", torch.int32, (b,))
+    dev = tree_token.device
+    acc_len = torch.empty((b,), dtype=torch.int32, device=dev)
+    acc_tok = torch.empty((b, int(max_accept)), dtype=torch.int32, device=dev)
+    acc_node = torch.empty((b, int(max_accept)), dtype=torch.int32, device=dev)
+    rc = kdtree_tree_accept(tree_token.data_ptr(), first_child.data_ptr(), next_sibling.data_ptr(),
+                            q_len.data_ptr(), target_next.data_ptr(), b, n, int(max_accept),
+                            acc_len.data_ptr(), acc_tok.data_ptr(), acc_node.data_ptr(),
+                            torch.cuda.current_stream(dev).cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"kdtree_tree_accept failed: {rc} ({ERRORS.get(rc, '?')})")
+    return acc_len, acc_tok, acc_node
 def choose_num_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
                       n_cu: int = 256, rows_per_block: int = 128, min_chunk: int = 512) -> int:
     """Host-side split-KV heuristic for callers that know their prefix lengths: enough

@@ -174,4 +174,53 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
   return launch_attend(p, dtype, (hipStream_t)stream);
 }
 
+int32_t kdtree_build_ddtree(const float* logp, const int32_t* token_ids,
+                            const int32_t* root_token, int32_t batch, int32_t depth,
+                            int32_t top_k, int32_t budget, int32_t* q_len, int32_t* tree_parent,
+                            int32_t* tree_token, int32_t* tree_depth, int32_t* first_child,
+                            int32_t* next_sibling, float* tree_score, void* stream) {
+  if (!logp || !token_ids || !root_token || !q_len || !tree_parent || !tree_token ||
+      !tree_depth || !first_child || !next_sibling)
+    return KDTREE_ERR_NULL;
+  if (batch < 1 || depth < 1 || depth > kdt::MAX_DDTREE_DEPTH || top_k < 1 || top_k > 4095 ||
+      (int64_t)depth * top_k > kdt::MAX_DDTREE_TABLE || budget < 0 ||
+      budget > kdt::MAX_DDTREE_BUDGET)
+    return KDTREE_ERR_SHAPE;
+  kdt::DdtreeBuildParams p{logp, token_ids, root_token, batch, depth, top_k, budget, q_len,
+                           tree_parent, tree_token, tree_depth, first_child, next_sibling,
+                           tree_score};
+  return kdt::launch_build_ddtree(p, (hipStream_t)stream) == hipSuccess ? KDTREE_OK
+                                                                         : KDTREE_ERR_LAUNCH;
+}
+
+int32_t kdtree_tree_accept(const int32_t* tree_token, const int32_t* first_child,
+                           const int32_t* next_sibling, const int32_t* q_len,
+                           const int32_t* target_next, int32_t batch, int32_t max_nodes,
+                           int32_t max_accept, int32_t* accept_len, int32_t* accept_tokens,
+                           int32_t* accept_nodes, void* stream) {
+  if (!tree_token || !first_child || !next_sibling || !q_len || !target_next || !accept_len ||
+      !accept_tokens || !accept_nodes)
+    return KDTREE_ERR_NULL;
+  if (batch < 1 || max_nodes < 1 || max_nodes > (1 << 20) || max_accept < 1 ||
+      max_accept > (1 << 20))
+    return KDTREE_ERR_SHAPE;
+  kdt::AcceptParams p{tree_token, first_child, next_sibling, q_len, target_next, batch,
+                      max_nodes, max_accept, accept_len, accept_tokens, accept_nodes};
+  return kdt::launch_tree_accept(p, (hipStream_t)stream) == hipSuccess ? KDTREE_OK
+                                                                        : KDTREE_ERR_LAUNCH;
+}
+
+int32_t kdtree_pack_tree(const int32_t* q_len, const int32_t* tree_parent,
+                         const int32_t* tree_token, int32_t batch, int32_t width, int64_t total_q,
+                         int32_t* packed_parent, int32_t* packed_token, int64_t* q_offsets,
+                         void* stream) {
+  if (!q_len || !tree_parent || !packed_parent || (packed_token && !tree_token))
+    return KDTREE_ERR_NULL;
+  if (batch < 1 || width < 1 || width > (1 << 20) || total_q < 1) return KDTREE_ERR_SHAPE;
+  kdt::PackParams p{q_len,   tree_parent,   tree_token,   batch,    width,
+                    total_q, packed_parent, packed_token, q_offsets};
+  return kdt::launch_pack_tree(p, (hipStream_t)stream) == hipSuccess ? KDTREE_OK
+                                                                      : KDTREE_ERR_LAUNCH;
+}
+
 }  // extern "C"

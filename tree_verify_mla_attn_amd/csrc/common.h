@@ -42,7 +42,52 @@ struct VerifyParams {
   int64_t k16_tiles; // capacity of `k16` in tiles
 };
 
+// Draft-tree builder and accept.
+constexpr int MAX_DDTREE_BUDGET = 64;     // drafted nodes per tree (q_len <= 65)
+constexpr int MAX_DDTREE_DEPTH = 64;
+constexpr int MAX_DDTREE_TABLE = 4096;    // depth * top_k entries of one request's table
+
+struct DdtreeBuildParams {
+  const float* logp;          // [batch, depth, top_k]
+  const int32_t* token_ids;   // [batch, depth, top_k]
+  const int32_t* root_token;  // [batch]
+  int32_t batch, depth, top_k, budget;
+  int32_t* q_len;             // [batch]
+  int32_t* tree_parent;       // [batch, budget + 1] (all five)
+  int32_t* tree_token;
+  int32_t* tree_depth;
+  int32_t* first_child;
+  int32_t* next_sibling;
+  float* tree_score;          // nullable
+};
+
+struct AcceptParams {
+  const int32_t* tree_token;    // [batch, max_nodes] (also the two pointer arrays)
+  const int32_t* first_child;
+  const int32_t* next_sibling;
+  const int32_t* q_len;         // [batch]
+  const int32_t* target_next;   // [batch, max_nodes]
+  int32_t batch, max_nodes, max_accept;
+  int32_t* accept_len;          // [batch]
+  int32_t* accept_tokens;       // [batch, max_accept]
+  int32_t* accept_nodes;        // [batch, max_accept]
+};
+
+struct PackParams {
+  const int32_t* q_len;         // [batch]
+  const int32_t* tree_parent;   // [batch, width]
+  const int32_t* tree_token;    // [batch, width] (nullable, with packed_token)
+  int32_t batch, width;
+  int64_t total_q;              // rows of the packed outputs
+  int32_t* packed_parent;       // [total_q]
+  int32_t* packed_token;        // [total_q] (nullable)
+  int64_t* q_offsets;           // [batch + 1] (nullable)
+};
+
 // Host-side launchers (defined in the .hip files).
+hipError_t launch_pack_tree(const PackParams& p, hipStream_t stream);
+hipError_t launch_build_ddtree(const DdtreeBuildParams& p, hipStream_t stream);
+hipError_t launch_tree_accept(const AcceptParams& p, hipStream_t stream);
 hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_verify_f32(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStream_t stream);
