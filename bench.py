@@ -12,6 +12,9 @@ Prints ONE JSON line (rank 0):
                PFLOP/s), from HIP events recorded on the launch stream around it in
                every timed step (the call is issued as its two phases for that)
   cpu_baseline = the float64 oracle on a bounded sample of the same workload
+  greedy_step  = per-launch device time of the draft-tree build, tree packing and greedy
+               accept kernels at the workload's tree shape (graph-replayed), beside the
+               host heap oracle's build time for the same batch
 """
 import argparse
 import json
@@ -72,6 +75,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-greedy-step", action="store_true",
+                    help="skip timing the tree build / pack / accept kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -109,6 +114,92 @@ def cpu_baseline(inp, seconds):
             "sample": f"float64 numpy oracle on the first {done} of {inp.batch} requests "
                       f"({flops:.3e} algorithmic FLOPs in {dt:.2f} s, BLAS threads={threads}, "
                       f"host cpus={os.cpu_count()})"}
+
+
+def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle=True):
+    """Per-launch device time of the steps around verify attention (draft-tree build, tree
+    packing, greedy accept) at a workload's tree shape, each as `reps` launches captured
+    in one HIP graph and replayed `replays` times between two events."""
+    import numpy as np
+    c = synth.CONFIGS[cfg]
+    rng = np.random.default_rng(1000 + cfg)
+    batch, budget = c["batch"], c["budget"]
+    ks = list(c["top_k"])
+    ks = ks * (batch // len(ks)) if len(ks) != batch else ks
+    logp, ids, root = synth.draft_tables(rng, batch, ks, depth=synth.MAX_DEPTH)
+    d_logp = torch.from_numpy(logp).to(dev)
+    d_ids = torch.from_numpy(ids).to(dev)
+    d_root = torch.from_numpy(root).to(dev)
+    t = B.build_ddtree(d_logp, d_ids, d_root, budget, with_score=False)
+    torch.cuda.synchronize(dev)
+    par, tok, ql = (t[k].cpu().numpy() for k in ("parent", "token", "q_len"))
+    width = budget + 1
+    tn = np.stack([synth.target_next_tokens(rng, par[b, :ql[b]], tok[b, :ql[b]], 0.8, width)
+                   for b in range(batch)])
+    d_tn = torch.from_numpy(tn).to(dev)
+    i32 = torch.int32
+    o = {k: torch.empty((batch, width), dtype=i32, device=dev)
+         for k in ("parent", "token", "depth", "first_child", "next_sibling")}
+    o_q = torch.empty((batch,), dtype=i32, device=dev)
+    pk_par = torch.empty((batch * width,), dtype=i32, device=dev)
+    pk_off = torch.empty((batch + 1,), dtype=torch.int64, device=dev)
+    a_len = torch.empty((batch,), dtype=i32, device=dev)
+    a_tok = torch.empty((batch, 16), dtype=i32, device=dev)
+    a_node = torch.empty((batch, 16), dtype=i32, device=dev)
+
+    def build(s):
+        return B.kdtree_build_ddtree(d_logp.data_ptr(), d_ids.data_ptr(), d_root.data_ptr(),
+                                     batch, logp.shape[1], logp.shape[2], budget, o_q.data_ptr(),
+                                     o["parent"].data_ptr(), o["token"].data_ptr(),
+                                     o["depth"].data_ptr(), o["first_child"].data_ptr(),
+                                     o["next_sibling"].data_ptr(), 0, s)
+
+    def pack(s):
+        return B.kdtree_pack_tree(o_q.data_ptr(), o["parent"].data_ptr(), 0, batch, width,
+                                  batch * width, pk_par.data_ptr(), 0, pk_off.data_ptr(), s)
+
+    def accept(s):
+        return B.kdtree_tree_accept(o["token"].data_ptr(), o["first_child"].data_ptr(),
+                                    o["next_sibling"].data_ptr(), o_q.data_ptr(), d_tn.data_ptr(),
+                                    batch, width, 16, a_len.data_ptr(), a_tok.data_ptr(),
+                                    a_node.data_ptr(), s)
+
+    res = {"workload": c["name"], "batch": batch, "budget": budget, "depth": synth.MAX_DEPTH,
+           "top_k": "per request, as the workload's trees"}
+    for name, fn in (("build", build), ("pack", pack), ("accept", accept)):
+        cs = torch.cuda.Stream(device=dev)
+        cs.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cs):
+            assert fn(cs.cuda_stream) == 0
+        torch.cuda.current_stream(dev).wait_stream(cs)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream(dev).cuda_stream
+            for _ in range(reps):
+                assert fn(s) == 0
+        g.replay()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        res[f"{name}_us"] = round(e0.elapsed_time(e1) * 1e3 / (reps * replays), 3)
+    acc = a_len.cpu().numpy()
+    res["mean_accept_len"] = round(float(acc.mean()), 3)
+    if cpu_oracle:
+        from oracle import ddtree_f32 as O  # the host heap the device builder replaces
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 1.0:
+            O.build_ddtree_batch(logp, ids, root, budget)
+            n += 1
+        res["cpu_baseline_build_us"] = {"value": round((time.perf_counter() - t0) * 1e6 / n, 1),
+                                        "kind": "oracle", "cores": 1,
+                                        "sample": f"{n} whole-batch builds in about 1 s"}
+    return res
 
 
 def main():
@@ -217,6 +308,9 @@ def main():
               file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if not args.no_greedy_step:
+        res["greedy_step"] = greedy_step_timing(B, synth, torch, dev, args.workload,
+                                                cpu_oracle=args.cpu_seconds > 0)
     print(json.dumps(res), flush=True)
 
 

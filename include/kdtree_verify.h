@@ -179,6 +179,7 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
 #define KDTREE_MAX_BUDGET 64     /* drafted nodes per tree: q_len <= 65 */
 #define KDTREE_MAX_DEPTH 64      /* draft positions per request */
 #define KDTREE_MAX_TABLE 4096    /* depth * top_k of one request's candidate table */
+#define KDTREE_MAX_ACCEPT_NODES 4096  /* max_nodes of kdtree_tree_accept */
 
 /*
  * Best-first draft-tree builder on the device, one wavefront per request ("The Milestone
@@ -248,9 +249,10 @@ int32_t kdtree_pack_tree(const int32_t* q_len, const int32_t* tree_parent,
                          void* stream);
 
 /*
- * Greedy follow-verified-tree accept, one thread per request ("The Milestone Commit
- * ...", section "The Context", item 3: a walk over the verified tree's next-token and
- * next-sibling pointers).
+ * Greedy follow-verified-tree accept ("The Milestone Commit ...", section "The Context",
+ * item 3: a walk over the verified tree's next-token and next-sibling pointers, one
+ * thread per request there; here one wavefront per request stages the tree in LDS and
+ * resolves every node's matching child in parallel before the walk).
  *
  *   tree_token, first_child, next_sibling   device int32 [batch, max_nodes], as written
  *               by kdtree_build_ddtree (max_nodes = budget + 1).
@@ -271,8 +273,8 @@ int32_t kdtree_pack_tree(const int32_t* q_len, const int32_t* tree_parent,
  *                  token, then -1.
  *   accept_nodes   device int32 [batch, max_accept]: node index of each accepted token,
  *                  -1 for the bonus token and the padding.
- * Returns as kdtree_build_ddtree (KDTREE_ERR_SHAPE: batch, max_nodes or max_accept < 1
- * or > 2^20).
+ * Returns as kdtree_build_ddtree (KDTREE_ERR_SHAPE: batch < 1, max_nodes outside
+ * [1, KDTREE_MAX_ACCEPT_NODES] or max_accept outside [1, 2^20]).
  */
 int32_t kdtree_tree_accept(const int32_t* tree_token, const int32_t* first_child,
                            const int32_t* next_sibling, const int32_t* q_len,

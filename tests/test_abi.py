@@ -144,12 +144,14 @@ def test_build_bad_shape_rejected(kw):
 
 def test_build_limits_match_header():
     text = open(HEADER).read()
-    for name in ("KDTREE_MAX_BUDGET", "KDTREE_MAX_DEPTH", "KDTREE_MAX_TABLE"):
+    for name in ("KDTREE_MAX_BUDGET", "KDTREE_MAX_DEPTH", "KDTREE_MAX_TABLE",
+                 "KDTREE_MAX_ACCEPT_NODES"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == getattr(B, name)
     src = open(os.path.join(ROOT, "tree_verify_mla_attn_amd", "csrc", "common.h")).read()
     for name, c in (("KDTREE_MAX_BUDGET", "MAX_DDTREE_BUDGET"), ("KDTREE_MAX_DEPTH", "MAX_DDTREE_DEPTH"),
-                    ("KDTREE_MAX_TABLE", "MAX_DDTREE_TABLE")):
+                    ("KDTREE_MAX_TABLE", "MAX_DDTREE_TABLE"),
+                    ("KDTREE_MAX_ACCEPT_NODES", "MAX_ACCEPT_NODES")):
         m = re.search(rf"constexpr int {c} = (\d+);", src)
         assert m and int(m.group(1)) == getattr(B, name)
 
@@ -169,7 +171,8 @@ def test_accept_null_pointer_rejected(field):
 
 
 @pytest.mark.parametrize("kw", [dict(batch=0), dict(max_nodes=0), dict(max_accept=0),
-                                dict(max_nodes=(1 << 20) + 1), dict(max_accept=(1 << 20) + 1)])
+                                dict(max_nodes=B.KDTREE_MAX_ACCEPT_NODES + 1),
+                                dict(max_accept=(1 << 20) + 1)])
 def test_accept_bad_shape_rejected(kw):
     assert _accept(**kw) == -2
 

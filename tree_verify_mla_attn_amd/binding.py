@@ -23,6 +23,7 @@ KDTREE_MAX_QLEN = 65
 KDTREE_MAX_BUDGET = 64
 KDTREE_MAX_DEPTH = 64
 KDTREE_MAX_TABLE = 4096
+KDTREE_MAX_ACCEPT_NODES = 4096
 KDTREE_DTYPE_FP32 = 0
 KDTREE_DTYPE_BF16 = 1
 ERRORS = {0: "OK", -1: "null pointer", -2: "bad shape", -3: "bad max_q_len", -4: "bad dtype",

@@ -201,7 +201,7 @@ int32_t kdtree_tree_accept(const int32_t* tree_token, const int32_t* first_child
   if (!tree_token || !first_child || !next_sibling || !q_len || !target_next || !accept_len ||
       !accept_tokens || !accept_nodes)
     return KDTREE_ERR_NULL;
-  if (batch < 1 || max_nodes < 1 || max_nodes > (1 << 20) || max_accept < 1 ||
+  if (batch < 1 || max_nodes < 1 || max_nodes > kdt::MAX_ACCEPT_NODES || max_accept < 1 ||
       max_accept > (1 << 20))
     return KDTREE_ERR_SHAPE;
   kdt::AcceptParams p{tree_token, first_child, next_sibling, q_len, target_next, batch,

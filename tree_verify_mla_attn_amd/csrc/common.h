@@ -46,6 +46,7 @@ struct VerifyParams {
 constexpr int MAX_DDTREE_BUDGET = 64;     // drafted nodes per tree (q_len <= 65)
 constexpr int MAX_DDTREE_DEPTH = 64;
 constexpr int MAX_DDTREE_TABLE = 4096;    // depth * top_k entries of one request's table
+constexpr int MAX_ACCEPT_NODES = 4096;    // nodes per tree the accept stages in LDS
 
 struct DdtreeBuildParams {
   const float* logp;          // [batch, depth, top_k]
