@@ -179,3 +179,78 @@ def test_planted_mistakes_fail_the_pins(monkeypatch):
     t = D.build_ddtree(lp, np.zeros(lp.shape, np.int32), 0, 3)
     monkeypatch.undo()
     assert np.float32(t["score"][3]) != np.float32(-1.0 - 2 * 2.0 ** -23)
+
+
+def _mutant(old, new):
+    """A copy of the oracle module with one planted mistake (source text replaced)."""
+    import inspect
+    import types
+    src = inspect.getsource(D)
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("ddtree_mutant")
+    exec(compile(src.replace(old, new), "ddtree_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _builder_pins_pass(mod):
+    for depth, k, budget, seed in [(3, 3, 10, 0), (4, 2, 15, 1), (2, 5, 12, 2), (5, 2, 31, 3)]:
+        logp = synth.logprob_table(np.random.default_rng(seed), k, depth).astype(np.float32)
+        t = mod.build_ddtree(logp, np.zeros((depth, k), np.int32), 7, budget)
+        if _tree_paths(t) != _brute_force_order(logp, budget):
+            return False
+        for i in range(1, len(t["parent"])):  # scores are the float32 path sums
+            ranks = _tree_paths(t)[i - 1]
+            s = np.float32(0.0)
+            for d, r in enumerate(ranks):
+                s = np.float32(s + logp[d, r])
+            if s != t["score"][i]:
+                return False
+    return True
+
+
+def _accept_pins_pass(mod):
+    for seed in range(6):
+        rng = np.random.default_rng(100 + seed)
+        lp, ids, root = synth.draft_tables(rng, 1, [8, 2, 4, 3, 2, 6][seed])
+        t = D.build_ddtree(lp[0], ids[0], root[0], 64)
+        tn = synth.target_next_tokens(rng, t["parent"], t["token"], 0.85, len(t["parent"]))
+        got = mod.tree_accept(t["token"], t["first_child"], t["next_sibling"], tn)
+        if got != _brute_force_accept(t["parent"], t["token"], tn):
+            return False
+    return True
+
+
+def test_unmodified_oracle_passes_the_mutation_harness():
+    assert _builder_pins_pass(D) and _accept_pins_pass(D)
+
+
+@pytest.mark.parametrize("old,new", [
+    # the first child pushed under the parent instead of the popped node
+    ("push(np.float32(score[node] + lp[d, 0]), d + 1, 0, node)",
+     "push(np.float32(score[node] + lp[d, 0]), d + 1, 0, p)"),
+    # the child scored from the parent's score
+    ("push(np.float32(score[node] + lp[d, 0]), d + 1, 0, node)",
+     "push(np.float32(score[p] + lp[d, 0]), d + 1, 0, node)"),
+    # the sibling scored with its own rank's log-probability
+    ("push(np.float32(score[p] + lp[d - 1, r + 1]), d, r + 1, p)",
+     "push(np.float32(score[p] + lp[d - 1, r]), d, r + 1, p)"),
+    # heap order by lowest score
+    ("heapq.heappush(heap, (-float(s), counter, d, r, p))",
+     "heapq.heappush(heap, (float(s), counter, d, r, p))"),
+])
+def test_planted_builder_mistakes_fail(old, new):
+    assert not _builder_pins_pass(_mutant(old, new))
+
+
+@pytest.mark.parametrize("old,new", [
+    # the walk takes the first child whatever its token
+    ("while c >= 0 and int(token[c]) != want:", "while False:"),
+    # the bonus token taken from the current node instead of the target
+    ("tokens.append(want)  # bonus token: the target's own next token",
+     "tokens.append(int(token[cur]))"),
+    # the walk stops one step early
+    ("        nodes.append(c)\n        tokens.append(want)\n        cur = c",
+     "        nodes.append(c)\n        tokens.append(want)\n        cur = c\n        tokens.append(int(target_next[cur]))\n        return nodes, tokens"),
+])
+def test_planted_accept_mistakes_fail(old, new):
+    assert not _accept_pins_pass(_mutant(old, new))
