@@ -348,22 +348,22 @@ __device__ __forceinline__ uint32_t tile_visibility(int key0, int key_begin, int
 
 // Online softmax of one tile: S^T (raw scores, register r <-> key 8(r/4) + 4h + r%4)
 // -> P (fp16) and the running max / sum.  `vis` = visibility bits (see above).
+// The scale c (> 0: the prologue folds a sign or a zero scale into Q) is applied inside
+// the exponent's argument, exp2(s c - m) as one fma.  The row max of the raw scores
+// times c is exactly the max of the rounded products, since rounding is monotone; masked
+// keys stay -inf.
 __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState& st, float c,
                                              bool masked, uint32_t vis, int lane) {
   const int h = lane >> 5;
   if (masked) {
     const uint32_t vh = vis >> (4 * h);
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      s[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] * c : -INFINITY;
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = s[r] * c;
+    for (int r = 0; r < 16; ++r) s[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
   }
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = pair_max(mx);
+  mx = pair_max(mx) * c;
   // Lazy rescale: the running max only moves when this tile beats it by more than
   // 2^RESCALE_THRESHOLD; the caller then scales O by `alpha` (rare after the first tile).
   const bool need = mx > st.m + RESCALE_THRESHOLD;  // also true when st.m == -inf
@@ -381,8 +381,8 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState
     u32x4 packed;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const float p0 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * d] - mref);
-      const float p1 = __builtin_amdgcn_exp2f(s[8 * kk + 2 * d + 1] - mref);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + 2 * d], c, -mref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + 2 * d + 1], c, -mref));
       // round to nearest even (one v_cvt_pk_f16_f32); l sums the rounded values
       const f16x2 hp = {(_Float16)p0, (_Float16)p1};
       st.l = __builtin_amdgcn_fdot2(hp, ones, st.l, false);
@@ -574,6 +574,15 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
         qf[ks][d] = __builtin_bit_cast(unsigned, hp);
       }
     }
+    // The softmax takes a positive scale.  A negative one is moved into Q by flipping
+    // every sign bit (exact: each score is then exactly negated); a zero one by zeroing
+    // Q (every score is then exactly 0) with scale 1.
+    const unsigned flip = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
+    const unsigned keep = p.scale_log2 == 0.0f ? 0u : 0xffffffffu;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) qf[ks][d] = (qf[ks][d] & keep) ^ flip;
   }
 
   const char* k_rope = (const char*)p.k_rope + kvoff * (DR * 2);  // this request's rows
@@ -585,7 +594,7 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const int key_last = k_end - 1;
   const int n_tiles = (k_end - k_begin + BN - 1) / BN;
   const int mask_from = min(P, k_end);  // tiles ending at or before this key are unmasked
-  const float c = p.scale_log2;
+  const float c = p.scale_log2 > 0.0f ? p.scale_log2 : (p.scale_log2 < 0.0f ? -p.scale_log2 : 1.0f);
 
   f32x16 o[16];
 #pragma unroll
