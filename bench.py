@@ -14,7 +14,8 @@ Prints ONE JSON line (rank 0):
   cpu_baseline = the float64 oracle on a bounded sample of the same workload
   greedy_step  = per-launch device time of the draft-tree build, tree packing and greedy
                accept kernels at the workload's tree shape (graph-replayed), beside the
-               host heap oracle's build time for the same batch
+               host heap oracle's build time for the same batch; step_us = the whole
+               build -> pack -> verify -> accept chain as one graph
 """
 import argparse
 import json
@@ -116,7 +117,8 @@ def cpu_baseline(inp, seconds):
                       f"host cpus={os.cpu_count()})"}
 
 
-def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle=True):
+def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle=True,
+                       verify=None):
     """Per-launch device time of the steps around verify attention (draft-tree build, tree
     packing, greedy accept) at a workload's tree shape, each as `reps` launches captured
     in one HIP graph and replayed `replays` times between two events."""
@@ -189,6 +191,37 @@ def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle
         res[f"{name}_us"] = round(e0.elapsed_time(e1) * 1e3 / (reps * replays), 3)
     acc = a_len.cpu().numpy()
     res["mean_accept_len"] = round(float(acc.mean()), 3)
+    if verify is not None:
+        # the whole step on the device: build -> pack -> verify attention over the built
+        # trees (the workload's q / kv rows, which its trees fill exactly) -> accept on
+        # fixed target tokens (the target model's argmax is outside this path)
+        vq, vqr, vkv, vkr, vprefix, vout, vlse, vws, vsplits, vscale = verify
+        if int(vq.shape[0]) != batch * width:
+            res["step_us"] = None
+        else:
+            def chain(s):
+                assert build(s) == 0 and pack(s) == 0
+                B.VerifyAttn()(vq, vqr, vkv, vkr, vprefix, pk_par, o_q, vscale, out_lat=vout,
+                               out_lse=vlse, num_splits=vsplits, max_q_len=width, workspace=vws)
+                assert accept(s) == 0
+            cs = torch.cuda.Stream(device=dev)
+            cs.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(cs):
+                chain(cs.cuda_stream)
+            torch.cuda.current_stream(dev).wait_stream(cs)
+            torch.cuda.synchronize(dev)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                chain(torch.cuda.current_stream(dev).cuda_stream)
+            g.replay()
+            torch.cuda.synchronize(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays * 4):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize(dev)
+            res["step_us"] = round(e0.elapsed_time(e1) * 1e3 / (replays * 4), 2)
     if cpu_oracle:
         from oracle import ddtree_f32 as O  # the host heap the device builder replaces
         t0 = time.perf_counter()
@@ -309,8 +342,10 @@ def main():
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     if not args.no_greedy_step:
-        res["greedy_step"] = greedy_step_timing(B, synth, torch, dev, args.workload,
-                                                cpu_oracle=args.cpu_seconds > 0)
+        res["greedy_step"] = greedy_step_timing(
+            B, synth, torch, dev, args.workload, cpu_oracle=args.cpu_seconds > 0,
+            verify=(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], out, lse,
+                    ws, splits, inp.scale))
     print(json.dumps(res), flush=True)
 
 
