@@ -272,3 +272,56 @@ def test_prepare_then_attend(dev, dtype):
     out, lse = call(*args, num_splits=4, max_q_len=65, workspace=ws, mid_event=mid)
     torch.cuda.synchronize(dev)
     assert torch.equal(out, ref[4][0]) and torch.equal(lse, ref[4][1])
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_flagged_request_rows_left_unwritten(dev, splits):
+    """A request flagged on the device keeps its output rows; the others are unchanged."""
+    base = EDGE["ragged_batch5_h64"]("bf16")
+    bad_parent = base.tree_parent.copy()
+    bad_parent[3] = 7  # request 1, node 2: a parent must precede its node
+    inp = synth.VerifyInputs(**{**base.__dict__, "tree_parent": bad_parent})
+    h = inp.num_heads
+    outs = {}
+    for name, x in (("clean", base), ("bad", inp)):
+        d = synth.device_tensors(x, dev)
+        out = torch.full((x.total_q, h, 512), 7.25, dtype=torch.float32, device=dev)
+        lse = torch.full((x.total_q, h), 7.25, dtype=torch.float32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        print(f"case flagged/{name} splits={splits}", flush=True)
+        B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+                      d["tree_parent"], d["q_len"], x.scale, out_lat=out, out_lse=lse,
+                      num_splits=splits, max_q_len=65, status=status)
+        torch.cuda.synchronize(dev)
+        outs[name] = (out.cpu(), lse.cpu(), int(status.item()))
+    assert outs["clean"][2] == 0 and outs["bad"][2] & 4
+    q0 = int(base.q_len[0])
+    q1 = q0 + int(base.q_len[1])
+    assert (outs["bad"][0][q0:q1] == 7.25).all() and (outs["bad"][1][q0:q1] == 7.25).all()
+    for a, b in ((outs["bad"][0], outs["clean"][0]), (outs["bad"][1], outs["clean"][1])):
+        assert torch.equal(a[:q0], b[:q0]) and torch.equal(a[q1:], b[q1:])
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_rows_past_the_packed_total_left_unwritten(dev, splits):
+    """total_q larger than sum(q_len): the spare output rows keep their contents."""
+    inp = EDGE["ragged_batch5_h64"]("bf16")
+    d = synth.device_tensors(inp, dev)
+    extra = 3
+    h = inp.num_heads
+
+    def pad(t, fill):
+        tail = torch.full((extra,) + tuple(t.shape[1:]), fill, dtype=t.dtype, device=dev)
+        return torch.cat([t, tail]).contiguous()
+    q_lat, q_rope = pad(d["q_lat"], 0.5), pad(d["q_rope"], 0.5)
+    parent = pad(d["tree_parent"], -1)
+    out = torch.full((inp.total_q + extra, h, 512), 7.25, dtype=torch.float32, device=dev)
+    lse = torch.full((inp.total_q + extra, h), 7.25, dtype=torch.float32, device=dev)
+    print(f"case spare_rows splits={splits}", flush=True)
+    B.verify_attn(q_lat, q_rope, d["kv_lat"], d["k_rope"], d["prefix_len"], parent, d["q_len"],
+                  inp.scale, out_lat=out, out_lse=lse, num_splits=splits, max_q_len=65)
+    torch.cuda.synchronize(dev)
+    assert (out[inp.total_q:] == 7.25).all() and (lse[inp.total_q:] == 7.25).all()
+    r_out, r_lse = verify_attn_inputs(inp)
+    check(f"spare_rows/{splits}", inp, out[:inp.total_q].double().cpu().numpy(),
+          lse[:inp.total_q].double().cpu().numpy(), r_out, r_lse)

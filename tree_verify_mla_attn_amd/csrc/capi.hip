@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kMaxSplits = 256;
+constexpr int32_t kMaxSplits = kdt::MAX_SPLITS;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -99,8 +99,14 @@ int32_t launch_prepare(const kdt::VerifyParams& p, const WorkspaceLayout& w, int
 }
 
 int32_t launch_attend(const kdt::VerifyParams& p, int32_t dtype, hipStream_t s) {
-  hipError_t e = dtype == KDTREE_DTYPE_BF16 ? kdt::launch_verify_bf16(p, s)
-                                            : kdt::launch_verify_f32(p, s);
+  hipError_t e = hipSuccess;
+  if (p.num_splits > 1) {
+    // partial lse = NaN until an attention kernel writes it: the merge leaves rows that
+    // no kernel wrote (skipped requests, rows past the packed total) unwritten
+    e = kdt::launch_fill_nan(p.part_lse, (int64_t)p.num_splits * p.total_q * p.num_heads, s);
+    if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
+  }
+  e = dtype == KDTREE_DTYPE_BF16 ? kdt::launch_verify_bf16(p, s) : kdt::launch_verify_f32(p, s);
   if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
   if (p.num_splits > 1) {
     e = kdt::launch_lse_merge(p.part_o, p.part_lse, p.out_lat, p.out_lse,

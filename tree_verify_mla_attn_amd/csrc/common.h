@@ -15,6 +15,7 @@ constexpr int TILE_KEYS = 32;              // keys per pre-converted fp16 latent
 constexpr int64_t TILE_BYTES = DL * TILE_KEYS * 2;
 constexpr int ORDER_MAX_BATCH = 4096;      // larger batches keep the request order as given
 constexpr int NUM_XCD = 8;                 // MI355X: workgroup i runs on XCD i % 8
+constexpr int MAX_SPLITS = 256;            // split-KV factor limit
 constexpr float LN2 = 0.69314718055994530942f;
 
 // Status bits (mirrors include/kdtree_verify.h).
@@ -92,6 +93,7 @@ hipError_t launch_tree_accept(const AcceptParams& p, hipStream_t stream);
 hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_verify_f32(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStream_t stream);
+hipError_t launch_fill_nan(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, float* out_lat,
                             float* out_lse, int64_t rows, int32_t num_splits, hipStream_t stream);
 int rows_per_block_bf16();
