@@ -1,0 +1,130 @@
+"""Pins of the CPU oracle for the temperature draw of the accept step.
+
+Generator: Philox4x64-10 against numpy's own implementation of it (an independent
+library routine).  Draw: frequencies over many rows against softmax(logits / T) (the
+Gumbel-max identity), the T -> 0 limit, -inf entries, and planted mistakes.
+"""
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+from oracle import ddtree_f32 as D
+from oracle import sample_f32 as S
+
+
+@pytest.mark.parametrize("key,ctr", [((0, 0), (0, 0, 0, 0)), ((123, 456), (7, 8, 9, 10)),
+                                     ((2**64 - 1, 2**63 + 5), (2**64 - 2, 1, 2**40, 3))])
+def test_philox_matches_numpy(key, ctr):
+    g = np.random.Philox(key=np.array(key, np.uint64), counter=np.array(ctr, np.uint64))
+    raw = g.random_raw(12)
+    for blk in range(3):  # numpy produces block k from counter + 1 + k
+        c0 = (ctr[0] + 1 + blk) % 2**64
+        carry = (ctr[0] + 1 + blk) // 2**64
+        c = (c0, ctr[1] + carry, ctr[2], ctr[3])
+        mine = S.philox4x64_10(tuple(np.array([v], np.uint64) for v in c), key)
+        assert [int(w[0]) for w in mine] == [int(x) for x in raw[4 * blk:4 * blk + 4]]
+
+
+def test_uniforms_open_interval_and_layout():
+    u = S.uniforms(3, 4096, seed=11, offset=5)
+    assert u.dtype == np.float32 and (u > 0).all() and (u < 1).all()
+    # entries 8k .. 8k+7 come from one generator block: the same counter (k, row)
+    x = S.philox4x64_10((np.array([2], np.uint64), np.array([3], np.uint64),
+                         np.array([0], np.uint64), np.array([0], np.uint64)), (11, 5))
+    for j in range(8):
+        x32 = (int(x[j // 2][0]) >> (32 * (j % 2))) & 0xFFFFFFFF
+        assert u[16 + j] == np.float32(((x32 >> 9) * 2 + 1) * 2.0 ** -24)
+    assert abs(float(u.mean()) - 0.5) < 0.02
+
+
+@pytest.mark.parametrize("temperature", [0.5, 1.0, 2.0])
+def test_frequencies_follow_softmax(temperature):
+    logits = np.array([1.0, 0.2, -0.5, 2.0, -3.0, 0.0], np.float32)
+    rows = 20000
+    tok = S.sample_tokens(np.tile(logits, (rows, 1)), temperature, seed=7, offset=int(temperature * 10))
+    counts = np.bincount(tok, minlength=6).astype(np.float64)
+    p = np.exp(logits.astype(np.float64) / temperature)
+    p /= p.sum()
+    expected = rows * p
+    chi2 = float(((counts - expected) ** 2 / expected).sum())
+    assert chi2 < 30.0, (chi2, counts, expected)  # 5 dof: p(chi2 > 30) ~ 1.5e-5
+
+
+def test_zero_temperature_is_argmax_and_small_temperature_converges():
+    rng = np.random.default_rng(3)
+    logits = rng.normal(0, 3, size=(50, 1000)).astype(np.float32)
+    np.testing.assert_array_equal(S.sample_tokens(logits, 0.0, 1, 2), np.argmax(logits, axis=1))
+    gap = np.sort(logits, axis=1)[:, -1] - np.sort(logits, axis=1)[:, -2]
+    ok = gap > 1e-2  # T = 1e-4 turns a gap of 1e-2 into 100, beyond any Gumbel variate here
+    got = S.sample_tokens(logits, 1e-4, 1, 2)
+    np.testing.assert_array_equal(got[ok], np.argmax(logits, axis=1)[ok])
+
+
+def test_masked_entries_never_drawn_and_all_masked_row():
+    logits = np.full((300, 8), -np.inf, np.float32)
+    logits[:, [2, 5]] = 0.0
+    logits[-1] = -np.inf
+    tok = S.sample_tokens(logits, 1.0, 9, 0)
+    assert set(tok[:-1].tolist()) == {2, 5} and tok[-1] == -1
+    assert S.sample_tokens(logits, 0.0, 9, 0)[-1] == -1
+
+
+def test_seed_and_offset_change_the_draw():
+    logits = np.zeros((200, 64), np.float32)
+    a = S.sample_tokens(logits, 1.0, 1, 0)
+    assert (a != S.sample_tokens(logits, 1.0, 2, 0)).mean() > 0.9
+    assert (a != S.sample_tokens(logits, 1.0, 1, 1)).mean() > 0.9
+    np.testing.assert_array_equal(a, S.sample_tokens(logits, 1.0, 1, 0))
+
+
+def test_temperature_walk_reduces_to_greedy_at_zero():
+    """The temperature accept is the greedy walk fed with drawn tokens."""
+    rng = np.random.default_rng(5)
+    lp = -np.sort(-rng.random((6, 3)).astype(np.float32), axis=1)
+    ids = np.arange(18, dtype=np.int32).reshape(6, 3)
+    t = D.build_ddtree(np.log(lp), ids, 99, 12)
+    n = len(t["parent"])
+    logits = rng.normal(size=(n, 18)).astype(np.float32)
+    for i in range(n):  # make the target favour one child where there is one
+        kids = [c for c in range(n) if t["parent"][c] == i]
+        if kids:
+            logits[i, t["token"][kids[0]]] += 5.0
+    drawn = S.sample_tokens(logits, 0.0, 0, 0)
+    assert D.tree_accept(t["token"], t["first_child"], t["next_sibling"], drawn) == \
+        D.tree_accept(t["token"], t["first_child"], t["next_sibling"], np.argmax(logits, 1))
+
+
+def _mutant(old, new):
+    src = inspect.getsource(S)
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("sample_mutant")
+    exec(compile(src.replace(old, new), "sample_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("old,new", [
+    ("(lg * inv_t)", "(lg * np.float32(temperature))"),          # T applied the wrong way
+    ("g = -np.log(-np.log(u))", "g = np.log(-np.log(u))"),       # Gumbel sign flipped
+    ("g = -np.log(-np.log(u))", "g = -np.log(u)"),               # not a Gumbel variate
+])
+def test_planted_mistakes_fail_the_frequency_pin(old, new):
+    mod = _mutant(old, new)
+    logits = np.array([1.0, 0.2, -0.5, 2.0, -3.0, 0.0], np.float32)
+    rows, temperature = 20000, 0.5
+    tok = mod.sample_tokens(np.tile(logits, (rows, 1)), temperature, seed=7, offset=5)
+    counts = np.bincount(tok, minlength=6).astype(np.float64)
+    p = np.exp(logits.astype(np.float64) / temperature)
+    p /= p.sum()
+    chi2 = float(((counts - rows * p) ** 2 / (rows * p)).sum())
+    assert chi2 > 30.0
+
+
+def test_planted_generator_mistake_fails_the_numpy_pin():
+    mod = _mutant("c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0",
+                  "c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k0, lo0")
+    g = np.random.Philox(key=np.array([123, 456], np.uint64), counter=np.array([7, 8, 9, 10], np.uint64))
+    raw = g.random_raw(4)
+    mine = mod.philox4x64_10(tuple(np.array([v], np.uint64) for v in (8, 8, 9, 10)), (123, 456))
+    assert [int(w[0]) for w in mine] != [int(x) for x in raw]
