@@ -20,10 +20,12 @@ Draw (T > 0), per row r and vocabulary entry i, all in float32 except the genera
           "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011), word (i // 2) % 4,
           low 32 bits for even i, high 32 bits for odd i
   u     = (2 * (x32 >> 9) + 1) * 2^-24, in (0, 1)
-  g     = -log(-log(u))                                  (a standard Gumbel variate)
-  z     = logit * (1 / T) + g                            (each operation rounded)
+  c     = log2(e) / T                                    (float32 constants, rounded)
+  z     = logit * c - log2(-log2(u))                     (each operation rounded)
   token = argmax_i z, lowest i on ties; -1 if every logit is -inf.
-The Gumbel-max identity makes token ~ softmax(logit / T).  T = 0: token = argmax_i logit.
+z is log2(e) times the Gumbel-max key logit / T - ln(-ln u), less the constant
+log2(ln 2): the same argmax, so token ~ softmax(logit / T) (the Gumbel-max identity), with
+base-2 logarithms throughout.  T = 0: token = argmax_i logit.
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ M0 = np.uint64(0xD2E7470EE14C6C93)
 M1 = np.uint64(0xCA5A826395121157)
 W0 = np.uint64(0x9E3779B97F4A7C15)
 W1 = np.uint64(0xBB67AE8584CAA73B)
+LOG2E = np.float32(1.4426950408889634)
 _LO = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
@@ -91,11 +94,11 @@ def perturbed(logits: np.ndarray, temperature: float, rows, seed: int, offset: i
     """z of the given rows (float32), as the module docstring defines it; logits holds
     those rows' values ([vocab] for one row index, [len(rows), vocab] for several)."""
     lg = np.asarray(logits, np.float32)
-    inv_t = np.float32(1.0) / np.float32(temperature)
+    c = np.float32(LOG2E) / np.float32(temperature)
     u = uniforms(rows, lg.shape[-1], seed, offset)
-    g = -np.log(-np.log(u))
+    g = np.log2(-np.log2(u))
     with np.errstate(invalid="ignore"):
-        return (lg * inv_t).astype(np.float32) + g.astype(np.float32)
+        return (lg * c).astype(np.float32) - g.astype(np.float32)
 
 
 def sample_tokens(logits: np.ndarray, temperature: float, seed: int, offset: int,

@@ -2,7 +2,8 @@
 
 Generator: Philox4x64-10 against numpy's own implementation of it (an independent
 library routine).  Draw: frequencies over many rows against softmax(logits / T) (the
-Gumbel-max identity), the T -> 0 limit, -inf entries, and planted mistakes.
+Gumbel-max identity, here in base-2 form), the T -> 0 limit, -inf entries, and planted
+mistakes.
 """
 import inspect
 import types
@@ -105,9 +106,11 @@ def _mutant(old, new):
 
 
 @pytest.mark.parametrize("old,new", [
-    ("(lg * inv_t)", "(lg * np.float32(temperature))"),          # T applied the wrong way
-    ("g = -np.log(-np.log(u))", "g = np.log(-np.log(u))"),       # Gumbel sign flipped
-    ("g = -np.log(-np.log(u))", "g = -np.log(u)"),               # not a Gumbel variate
+    ("(lg * c)", "(lg * np.float32(temperature))"),               # T applied the wrong way
+    ("g = np.log2(-np.log2(u))", "g = -np.log2(-np.log2(u))"),   # Gumbel sign flipped
+    ("g = np.log2(-np.log2(u))", "g = np.log2(u)"),              # not a Gumbel variate
+    ("np.float32(LOG2E) / np.float32(temperature)",
+     "np.float32(1.0) / np.float32(temperature)"),               # base mismatch
 ])
 def test_planted_mistakes_fail_the_frequency_pin(old, new):
     mod = _mutant(old, new)
