@@ -15,7 +15,8 @@ Prints ONE JSON line (rank 0):
   greedy_step  = per-launch device time of the draft-tree build, tree packing and greedy
                accept kernels at the workload's tree shape (graph-replayed), beside the
                host heap oracle's build time for the same batch; step_us = the whole
-               build -> pack -> verify -> accept chain as one graph
+               build -> pack -> verify -> accept chain as one graph; sample_*_us = the
+               temperature draw over the full vocabulary at every node (HBM-bound)
 """
 import argparse
 import json
@@ -191,6 +192,29 @@ def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle
         res[f"{name}_us"] = round(e0.elapsed_time(e1) * 1e3 / (reps * replays), 3)
     acc = a_len.cpu().numpy()
     res["mean_accept_len"] = round(float(acc.mean()), 3)
+    # the temperature path's draw: the target's next token at every node from logits over
+    # the full vocabulary (synthetic N(0, 2) logits), fp32 and bf16, T = 0.8
+    for dt_name, dt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        logits = (torch.randn((batch * width, synth.VOCAB), device=dev) * 2.0).to(dt)
+        toks = torch.empty((batch * width,), dtype=i32, device=dev)
+        code = B.KDTREE_DTYPE_BF16 if dt == torch.bfloat16 else B.KDTREE_DTYPE_FP32
+
+        def draw(s, logits=logits, toks=toks, code=code):
+            return B.kdtree_sample_tokens(logits.data_ptr(), code, batch * width, synth.VOCAB,
+                                          synth.VOCAB, 0.8, 1234, 5, toks.data_ptr(), s)
+        assert draw(torch.cuda.current_stream(dev).cuda_stream) == 0
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            assert draw(torch.cuda.current_stream(dev).cuda_stream) == 0
+        e1.record()
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        nbytes = batch * width * synth.VOCAB * logits.element_size()
+        res[f"sample_{dt_name}_us"] = round(us, 2)
+        res[f"sample_{dt_name}_GBs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        del logits
     if verify is not None:
         # the whole step on the device: build -> pack -> verify attention over the built
         # trees (the workload's q / kv rows, which its trees fill exactly) -> accept on

@@ -282,6 +282,41 @@ int32_t kdtree_tree_accept(const int32_t* tree_token, const int32_t* first_child
                            int32_t max_accept, int32_t* accept_len, int32_t* accept_tokens,
                            int32_t* accept_nodes, void* stream);
 
+/*
+ * The target model's next token at every tree node, drawn at temperature T: the input of
+ * kdtree_tree_accept on the temperature path of the accept step ("The Milestone Commit
+ * ...", sections "Why This Message Was Written" and "How Decisions Were Made" name that
+ * sampling path without giving it).  The tree's candidates are the drafter's top-k,
+ * chosen rather than sampled, so the lossless accept draws the target's token at a node
+ * and follows the child that carries it: kdtree_tree_accept with these tokens as
+ * target_next.  T = 0 gives the greedy (argmax) tokens.
+ *
+ *   logits      device [rows, row_stride] of dtype KDTREE_DTYPE_FP32 or _BF16: the
+ *               target's logits at each node (entries [0, vocab) of a row are used).
+ *   rows        1 .. 2^31 - 1;  vocab >= 1;  row_stride >= vocab (elements).
+ *   temperature finite, >= 0.
+ *   seed, offset the generator key; draws of one (seed, offset) are reproducible, and
+ *               a caller advances offset per decoding step.
+ *   tokens      device int32 [rows]: the drawn token, or -1 if every logit is -inf.
+ *
+ * Draw of row r, T > 0: entry i takes u_i in (0, 1) from Philox4x64-10 (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) with counter (i / 8, r, 0, 0)
+ * and key (seed, offset): word (i / 2) % 4 of the block, low 32 bits for even i and high
+ * for odd i, x32 -> (2 (x32 >> 9) + 1) 2^-24.  With each step rounded in float32,
+ * z_i = logit_i * (log2(e) / T) - log2(-log2(u_i)), and the token is the argmax of z,
+ * lowest index on ties.  z is log2(e) times the Gumbel-max key logit / T - ln(-ln u)
+ * less a constant, so the token follows softmax(logit / T).  The logarithms are within
+ * about an ulp of the correctly rounded ones (the inner one relative to its value, as
+ * u near 1 decides the argmax).  T = 0: the argmax of the logits.  NaN logits are not
+ * allowed.
+ *
+ * Returns KDTREE_OK, KDTREE_ERR_NULL, KDTREE_ERR_SHAPE, KDTREE_ERR_DTYPE,
+ * KDTREE_ERR_SCALE (temperature negative or not finite) or KDTREE_ERR_LAUNCH.
+ */
+int32_t kdtree_sample_tokens(const void* logits, int32_t dtype, int64_t rows, int32_t vocab,
+                             int64_t row_stride, float temperature, uint64_t seed,
+                             uint64_t offset, int32_t* tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     names = _declared_functions()
     assert names == ["kdtree_build_ddtree", "kdtree_max_qlen", "kdtree_pack_tree",
-                     "kdtree_tree_accept",
+                     "kdtree_sample_tokens", "kdtree_tree_accept",
                      "kdtree_verify_attn", "kdtree_verify_attn_attend",
                      "kdtree_verify_attn_prepare", "kdtree_verify_attn_workspace_bytes"]
     for n in names:
@@ -194,3 +194,20 @@ def test_pack_null_pointer_rejected(kw):
                                 dict(total_q=0)])
 def test_pack_bad_shape_rejected(kw):
     assert _pack(**kw) == -2
+
+
+def _sample(**kw):
+    args = dict(logits=FAKE, dtype=0, rows=4, vocab=1000, row_stride=1000, temperature=1.0,
+                seed=1, offset=0, tokens=FAKE, stream=0)
+    args.update(kw)
+    return B.kdtree_sample_tokens(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=0), -1), (dict(tokens=0), -1),
+    (dict(rows=0), -2), (dict(rows=2 ** 31), -2), (dict(vocab=0), -2),
+    (dict(row_stride=999), -2), (dict(dtype=2), -4),
+    (dict(temperature=-0.5), -6), (dict(temperature=float("inf")), -6),
+    (dict(temperature=float("nan")), -6)])
+def test_sample_bad_arguments_rejected(kw, code):
+    assert _sample(**kw) == code

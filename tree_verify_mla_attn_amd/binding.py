@@ -68,6 +68,9 @@ def load_library():
                                         vp, vp]
     lib.kdtree_pack_tree.restype = i32
     lib.kdtree_pack_tree.argtypes = [vp, vp, vp, i32, i32, i64, vp, vp, vp, vp]
+    lib.kdtree_sample_tokens.restype = i32
+    lib.kdtree_sample_tokens.argtypes = [vp, i32, i64, i32, i64, ctypes.c_float, ctypes.c_uint64,
+                                         ctypes.c_uint64, vp, vp]
     lib.kdtree_tree_accept.restype = i32
     lib.kdtree_tree_accept.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
@@ -135,6 +138,14 @@ def kdtree_tree_accept(tree_token, first_child, next_sibling, q_len, target_next
         max_accept, accept_len, accept_tokens, accept_nodes, stream))
 
 
+def kdtree_sample_tokens(logits, dtype, rows, vocab, row_stride, temperature, seed, offset,
+                         tokens, stream) -> int:
+    """Raw call of the temperature draw (pointers as integer device addresses)."""
+    return int(load_library().kdtree_sample_tokens(logits, dtype, rows, vocab, row_stride,
+                                                   ctypes.c_float(temperature), seed, offset,
+                                                   tokens, stream))
+
+
 # ---------------------------------------------------------------- torch convenience
 def _check_dev(t, name, dtype, shape):
     import torch  # noqa: F401
@@ -199,6 +210,30 @@ def pack_tree(q_len, tree_parent, tree_token=None, total_q: Optional[int] = None
     if rc != 0:
         raise RuntimeError(f"kdtree_pack_tree failed: {rc} ({ERRORS.get(rc, '?')})")
     return packed_parent, packed_token, q_offsets
+
+
+def sample_tokens(logits, temperature: float, seed: int, offset: int = 0, vocab=None,
+                  tokens=None):
+    """The target's next token per row of logits [rows, >= vocab] (fp32 or bf16 on the GPU,
+    unit stride along the vocabulary) at temperature T (0 = argmax).  Returns int32
+    [rows] on the current stream."""
+    import torch
+    if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
+        raise ValueError("logits must be a GPU tensor [rows, vocab] with unit inner stride")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    rows = int(logits.shape[0])
+    vocab = int(logits.shape[1]) if vocab is None else int(vocab)
+    if tokens is None:
+        tokens = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    _check_dev(tokens, "tokens", torch.int32, (rows,))
+    dt = KDTREE_DTYPE_BF16 if logits.dtype == torch.bfloat16 else KDTREE_DTYPE_FP32
+    rc = kdtree_sample_tokens(logits.data_ptr(), dt, rows, vocab, int(logits.stride(0)),
+                              float(temperature), int(seed), int(offset), tokens.data_ptr(),
+                              torch.cuda.current_stream(logits.device).cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"kdtree_sample_tokens failed: {rc} ({ERRORS.get(rc, '?')})")
+    return tokens
 
 
 def tree_accept(tree_token, first_child, next_sibling, q_len, target_next, max_accept: int):

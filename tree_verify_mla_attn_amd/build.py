@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libkdtree_verify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["attn_bf16.hip", "attn_f32.hip", "prepass.hip", "merge.hip", "ddtree.hip", "capi.hip"]
+SOURCES = ["attn_bf16.hip", "attn_f32.hip", "prepass.hip", "merge.hip", "ddtree.hip", "sample.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

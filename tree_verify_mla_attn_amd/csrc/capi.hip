@@ -229,4 +229,20 @@ int32_t kdtree_pack_tree(const int32_t* q_len, const int32_t* tree_parent,
                                                                       : KDTREE_ERR_LAUNCH;
 }
 
+int32_t kdtree_sample_tokens(const void* logits, int32_t dtype, int64_t rows, int32_t vocab,
+                             int64_t row_stride, float temperature, uint64_t seed,
+                             uint64_t offset, int32_t* tokens, void* stream) {
+  if (!logits || !tokens) return KDTREE_ERR_NULL;
+  if (rows < 1 || rows > 0x7fffffff || vocab < 1 || row_stride < vocab ||
+      row_stride > ((int64_t)1 << 40) / (rows > 0 ? rows : 1))
+    return KDTREE_ERR_SHAPE;
+  if (dtype != KDTREE_DTYPE_FP32 && dtype != KDTREE_DTYPE_BF16) return KDTREE_ERR_DTYPE;
+  if (!(temperature >= 0.0f) || !(temperature < INFINITY)) return KDTREE_ERR_SCALE;
+  kdt::SampleParams p{logits, rows, row_stride, vocab, temperature, seed, offset, tokens};
+  return kdt::launch_sample_tokens(p, dtype == KDTREE_DTYPE_BF16, (hipStream_t)stream) ==
+                 hipSuccess
+             ? KDTREE_OK
+             : KDTREE_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -86,7 +86,17 @@ struct PackParams {
   int64_t* q_offsets;           // [batch + 1] (nullable)
 };
 
+struct SampleParams {
+  const void* logits;   // [rows, row_stride] fp32 or bf16
+  int64_t rows, row_stride;
+  int32_t vocab;
+  float temperature;    // >= 0 (0 = argmax)
+  uint64_t seed, offset;
+  int32_t* tokens;      // [rows]
+};
+
 // Host-side launchers (defined in the .hip files).
+hipError_t launch_sample_tokens(const SampleParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_pack_tree(const PackParams& p, hipStream_t stream);
 hipError_t launch_build_ddtree(const DdtreeBuildParams& p, hipStream_t stream);
 hipError_t launch_tree_accept(const AcceptParams& p, hipStream_t stream);

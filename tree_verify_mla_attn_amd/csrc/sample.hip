@@ -1,0 +1,169 @@
+// The target model's next token at every tree node, drawn at temperature T: the input of
+// the accept walk on the temperature path ("The Milestone Commit: Cementing Phase 1 ...",
+// sections "Why This Message Was Written" and "How Decisions Were Made": a sampling path
+// of the accept step, named but not given).  The tree's candidates are the drafter's
+// top-k, chosen rather than sampled, so the lossless accept draws the target's token at a
+// node and follows the child that carries it; this kernel does the draws, the walk is
+// the greedy accept kernel.
+//
+// Draw of row r (T > 0): entry i gets u_i in (0, 1) from Philox4x64-10 (Salmon et al.,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) with counter (i / 8, r, 0, 0)
+// and key (seed, offset): word (i / 2) % 4 of the block, its low 32 bits for even i and
+// high 32 bits for odd i, x32 -> (2 (x32 >> 9) + 1) 2^-24.  Then, rounding each step in
+// float32, z_i = logit_i * (log2(e) / T) - log2(-log2(u_i)), and the token is the argmax
+// of z, lowest index on ties.  z is log2(e) times the Gumbel-max key logit / T - ln(-ln u)
+// less a constant, so token ~ softmax(logit / T).  T = 0: argmax of the logits.  A row
+// whose logits are all -inf yields -1.
+//
+// HBM-bound: one workgroup per row streams the row once; a thread takes 8 consecutive
+// entries per step (one generator block), so every step of the workgroup reads a
+// contiguous 8 KB (fp32) or 4 KB (bf16).
+#include "common.h"
+
+namespace kdt {
+namespace {
+
+constexpr int SAMPLE_THREADS = 256;
+
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+  return __uint_as_float((unsigned)b << 16);
+}
+
+// 8 logits starting at entry i0 (entries at or past `vocab` read as -inf).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load8(const void* row, int64_t i0, int vocab, float (&x)[8]) {
+  if (VEC && i0 + 8 <= vocab) {
+    if constexpr (BF16) {
+      const uint4 v = *(const uint4*)((const unsigned short*)row + i0);
+      const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *(const float4*)((const float*)row + i0);
+      const float4 b = *(const float4*)((const float*)row + i0 + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t i = i0 + k;
+    if (i < vocab)
+      x[k] = BF16 ? bf16_to_f32(((const unsigned short*)row)[i]) : ((const float*)row)[i];
+    else
+      x[k] = -INFINITY;
+  }
+}
+
+// a * b - g with both operations rounded (never fused into one fma)
+__device__ __forceinline__ float mul_sub_rounded(float a, float b, float g) {
+#pragma clang fp contract(off)
+  const float ab = a * b;
+  return ab - g;
+}
+
+// (value, index) of the larger; equal values -> lower index; index -1 = nothing yet.
+__device__ __forceinline__ void keep_best(float& bz, int& bi, float z, int i) {
+  if (i < 0) return;
+  if (bi < 0 || z > bz || (z == bz && i < bi)) {
+    bz = z;
+    bi = i;
+  }
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SampleParams p) {
+  __shared__ float s_z[SAMPLE_THREADS / 64];
+  __shared__ int s_i[SAMPLE_THREADS / 64];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int vocab = p.vocab;
+  const void* row = (const char*)p.logits + r * p.row_stride * (BF16 ? 2 : 4);
+  float bz = -INFINITY;
+  int bi = -1;
+  const bool greedy = p.temperature == 0.0f;
+  const float cs = greedy ? 1.0f : __fdiv_rn(1.4426950408889634f, p.temperature);
+  for (int64_t g = tid; g * 8 < vocab; g += SAMPLE_THREADS) {
+    float x[8];
+    load8<BF16, VEC>(row, g * 8, vocab, x);
+    if (greedy) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (x[k] > bz) {  // entries rise within a thread: strict keeps the lowest index
+          bz = x[k];
+          bi = (int)(g * 8 + k);
+        }
+      continue;
+    }
+    uint64_t c[4] = {(uint64_t)g, (uint64_t)r, 0ull, 0ull};
+    philox4x64_10(c, p.seed, p.offset);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const unsigned x32 = (unsigned)(c[k >> 1] >> (32 * (k & 1)));
+      const float u = (float)((x32 >> 9) * 2u + 1u) * 0x1p-24f;
+      // the hardware base-2 log: within an ulp relative to the exact value over all u
+      // here, also near 1, where the small -log2(u) decide the argmax (u >= 2^-24 and
+      // -log2(u) >= 2^-24 / ln 2 are normal numbers)
+      const float gum = __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+      const float z = mul_sub_rounded(x[k], cs, gum);
+      if (z > bz) {
+        bz = z;
+        bi = (int)(g * 8 + k);
+      }
+    }
+  }
+  // -inf entries never win (bz starts at -inf, comparisons are strict)
+  for (int off = 32; off > 0; off >>= 1) {
+    const float oz = __shfl_xor(bz, off);
+    const int oi = __shfl_xor(bi, off);
+    keep_best(bz, bi, oz, oi);
+  }
+  if ((tid & 63) == 0) {
+    s_z[tid >> 6] = bz;
+    s_i[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < SAMPLE_THREADS / 64; ++w) keep_best(bz, bi, s_z[w], s_i[w]);
+    p.tokens[r] = bi;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sample_tokens(const SampleParams& p, bool bf16, hipStream_t stream) {
+  const size_t esize = bf16 ? 2 : 4;
+  const bool vec = ((uintptr_t)p.logits % 16 == 0) && ((p.row_stride * esize) % 16 == 0);
+  const dim3 grid((unsigned)p.rows), block(SAMPLE_THREADS);
+  if (bf16) {
+    if (vec) hipLaunchKernelGGL((sample_tokens_kernel<true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((sample_tokens_kernel<true, false>), grid, block, 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((sample_tokens_kernel<false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((sample_tokens_kernel<false, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kdt
