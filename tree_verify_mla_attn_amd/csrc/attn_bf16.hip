@@ -88,10 +88,17 @@ __device__ __forceinline__ void dma16(const char* uniform_base, unsigned lane_of
                                            0);
 }
 
-// One fp16 latent row (1 KB, already in its LDS image) per DMA.
-template <int S>
-__device__ __forceinline__ void dma_k16_row(const char* tile, int row, unsigned lane_off) {
-  dma16(tile + row * 1024, lane_off, k16<S>() + row * K16_ROW);
+// One fp16 latent row (1 KB, already in its LDS image) per DMA: row 8w + n of the tile
+// behind `rsrc` (one descriptor per tile), selected by the scalar offset (8w + n) KB.
+// (The immediate offset of an LDS-destination load moves the LDS address too, so it
+// stays 0.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* uniform_tile) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_tile, (short)0, -1, 0x00020000);
+}
+template <int S, int N>
+__device__ __forceinline__ void dma_k16_row(__amdgpu_buffer_rsrc_t rsrc, int wave, unsigned lane_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(k16<S>() + (wave * 8 + N) * K16_ROW),
+                                           16, (int)lane_off, (wave * 8 + N) * 1024, 0, 0);
 }
 
 // Rope rows 8w..8w+7 of keys [key0, key0+32) (clamped to key_last), one instruction per
@@ -113,8 +120,15 @@ __device__ __forceinline__ void issue_tile(const char* tile, const char* k_rope_
   // Re-materialise the lane id here so the per-lane offsets are recomputed per tile
   // instead of being hoisted out of the KV loop as long-lived registers.
   asm volatile("" : "+v"(lane));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dma_k16_row<S>(tile, wave * 8 + i, (unsigned)lane * 16u);
+  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(tile);
+  dma_k16_row<S, 0>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 1>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 2>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 3>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 4>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 5>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 6>(rsrc, wave, (unsigned)lane * 16u);
+  dma_k16_row<S, 7>(rsrc, wave, (unsigned)lane * 16u);
   dma_rope<S>(k_rope_req, key0, key_last, wave, lane);
 }
 
@@ -183,14 +197,23 @@ __device__ __forceinline__ f32x16 qk_dma(const u32x4 (&qf)[36], int lane, const 
   asm volatile("" : "+v"(dl));  // per-tile lane offsets, not hoisted out of the KV loop
   const int key0s = __builtin_amdgcn_readfirstlane(k_key0);
   const int lasts = __builtin_amdgcn_readfirstlane(key_last);
+  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(dma_tile);
 #pragma unroll
   for (int ks = 0; ks < 36; ++ks) {
     if (ks + 4 < 36) a[(ks + 4) & 7] = fr.get<SQ>(ks + 4, h);
     s = mfma_qk(ks, a[ks & 7], qf[ks], s);
     if ((ks & 3) == 3) {
-      const int n = ks >> 2;  // 0..8
-      if (n < 8) dma_k16_row<SD>(dma_tile, wave * 8 + n, (unsigned)dl * 16u);
-      else dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl);
+      switch (ks >> 2) {  // 0..8, resolved at compile time in the unrolled loop
+        case 0: dma_k16_row<SD, 0>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 1: dma_k16_row<SD, 1>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 2: dma_k16_row<SD, 2>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 3: dma_k16_row<SD, 3>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 4: dma_k16_row<SD, 4>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 5: dma_k16_row<SD, 5>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 6: dma_k16_row<SD, 6>(rsrc, wave, (unsigned)dl * 16u); break;
+        case 7: dma_k16_row<SD, 7>(rsrc, wave, (unsigned)dl * 16u); break;
+        default: dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl); break;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep each read four MFMAs ahead of its use
   }
