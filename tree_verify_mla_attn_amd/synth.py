@@ -243,12 +243,13 @@ def make_inputs(rng: np.random.Generator, *, num_heads: int, prefix_lens: Sequen
 # ------------------------------------------------------------------------ configs
 # The five workloads: batch, heads, prefix, draft budget / top-K, dtype, and the split-KV
 # launch configuration (workload 5 prescribes 16 chunks; the others use the count that
-# ran fastest on MI355X: small fp32 batches need splits to occupy the chip).
+# ran fastest on MI355X: small fp32 batches need splits to occupy the chip, and the best
+# counts keep the workgroups (row tiles x splits) within one round of the 256 CUs).
 CONFIGS = {
     1: dict(name="tiny_b1_p256_q9_fp32", batch=1, heads=64, prefix=256, top_k=[8], budget=8,
-            dtype="fp32", num_splits=8),
+            dtype="fp32", num_splits=12),
     2: dict(name="b1_p2048_q33_wide_fp32", batch=1, heads=64, prefix=2048, top_k=[8], budget=32,
-            dtype="fp32", num_splits=16),
+            dtype="fp32", num_splits=7),
     3: dict(name="b8_p4096_q65_deep_bf16", batch=8, heads=64, prefix=4096, top_k=[2], budget=64,
             dtype="bf16", num_splits=2),
     4: dict(name="b64_ragged1024-8192_q33_mixed_bf16", batch=64, heads=64, prefix=(1024, 8192),
