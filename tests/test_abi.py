@@ -115,9 +115,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 def test_choose_num_splits():
     # few row tiles + long prefixes -> more splits; many tiles -> none
-    assert B.choose_num_splits(1, 64, 33, 2081) >= 2
-    assert B.choose_num_splits(64, 64, 33, 5000) == 1
-    assert B.choose_num_splits(4, 64, 65, 32833) >= 2
+    # the counts a sweep on MI355X found fastest for the five workloads' shapes
+    assert B.choose_num_splits(1, 64, 33, 2081, dtype=B.KDTREE_DTYPE_FP32) == 7
+    assert 8 <= B.choose_num_splits(1, 64, 9, 265, dtype=B.KDTREE_DTYPE_FP32) <= 12
+    assert B.choose_num_splits(8, 64, 65, 4161) == 2
+    assert B.choose_num_splits(64, 64, 33, 4790) == 1
+    assert B.choose_num_splits(4, 64, 65, 32833) > 1
 
 
 # ---------------------------------------------------------------- builder and accept

@@ -260,14 +260,29 @@ def tree_accept(tree_token, first_child, next_sibling, q_len, target_next, max_a
         raise RuntimeError(f"kdtree_tree_accept failed: {rc} ({ERRORS.get(rc, '?')})")
     return acc_len, acc_tok, acc_node
 def choose_num_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
-                      n_cu: int = 256, rows_per_block: int = 128, min_chunk: int = 512) -> int:
-    """Host-side split-KV heuristic for callers that know their prefix lengths: enough
-    workgroups to cover the chip about twice, chunks of at least ``min_chunk`` keys."""
+                      dtype: int = KDTREE_DTYPE_BF16, n_cu: int = 256,
+                      overhead_keys: int = 800) -> int:
+    """Host-side split-KV choice for callers that know their prefix lengths.
+
+    One workgroup runs per CU, so a launch takes ceil(workgroups / n_cu) rounds, and a
+    round lasts about one split's keys (whole 32-key tiles) plus a fixed per-workgroup
+    cost of ~overhead_keys keys (the query fragment, pipeline start, output rows; fitted
+    on MI355X).  Returns the split count in 1..256 with the smallest
+    rounds * (chunk + overhead), the smallest count on ties.  It is a starting point, not
+    a measurement: it matches swept optima for short and medium prefixes, but for one
+    32768-key prefix per request it picks 7 where 16 ran 3.5% faster (smaller chunks keep
+    each split's keys within an XCD's L2)."""
+    rows_per_block = 128 if dtype == KDTREE_DTYPE_BF16 else 64
     blocks = batch * math.ceil(max_q_len * num_heads / rows_per_block)
-    s = 1
-    while s < 256 and blocks * s < 2 * n_cu and mean_kv / (2 * s) >= min_chunk:
-        s *= 2
-    return s
+    best, best_cost = 1, None
+    for s in range(1, 257):
+        chunk = math.ceil(math.ceil(mean_kv / s) / 32) * 32
+        cost = math.ceil(blocks * s / n_cu) * (chunk + overhead_keys)
+        if best_cost is None or cost < best_cost:
+            best, best_cost = s, cost
+        if chunk <= 32:
+            break
+    return best
 
 
 class VerifyAttn:
