@@ -16,7 +16,8 @@ Prints ONE JSON line (rank 0):
                accept kernels at the workload's tree shape (graph-replayed), beside the
                host heap oracle's build time for the same batch; step_us = the whole
                build -> pack -> verify -> accept chain as one graph; sample_*_us = the
-               temperature draw over the full vocabulary at every node (HBM-bound)
+               temperature draw over the full vocabulary at every node, on flat N(0, 2)
+               logits and on peaked (LM-like) ones
 """
 import argparse
 import json
@@ -194,8 +195,14 @@ def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle
     res["mean_accept_len"] = round(float(acc.mean()), 3)
     # the temperature path's draw: the target's next token at every node from logits over
     # the full vocabulary (synthetic N(0, 2) logits), fp32 and bf16, T = 0.8
-    for dt_name, dt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
-        logits = (torch.randn((batch * width, synth.VOCAB), device=dev) * 2.0).to(dt)
+    for dt_name, dt, peaked in (("fp32", torch.float32, False), ("bf16", torch.bfloat16, False),
+                                ("fp32_peaked", torch.float32, True),
+                                ("bf16_peaked", torch.bfloat16, True)):
+        logits = torch.randn((batch * width, synth.VOCAB), device=dev) * 2.0
+        if peaked:  # LM-like rows: an N(0, 2) bulk and 12 candidates near +24
+            top = torch.randint(0, synth.VOCAB, (batch * width, 12), device=dev)
+            logits.scatter_(1, top, 24.0 + 1.5 * torch.randn((batch * width, 12), device=dev))
+        logits = logits.to(dt)
         toks = torch.empty((batch * width,), dtype=i32, device=dev)
         code = B.KDTREE_DTYPE_BF16 if dt == torch.bfloat16 else B.KDTREE_DTYPE_FP32
 

@@ -85,6 +85,24 @@ def test_draw_matches_oracle_fp32(dev, temperature):
     compare("draw/fp32", logits, temperature, 1234, 7, got)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_draw_peaked_logits(dev, dtype):
+    """LM-like rows: a flat bulk and a few far higher candidates, so most blocks of 8
+    entries cannot hold the winner and the kernel skips their generator work; the draws
+    must still equal the oracle's (which evaluates every entry)."""
+    rng = np.random.default_rng(215)
+    logits = rng.normal(0, 2, size=(16, VOCAB)).astype(np.float32)
+    for r in range(16):
+        top = rng.choice(VOCAB, size=12, replace=False)
+        logits[r, top] = (18.0 if r % 2 else 24.0) + rng.normal(0, 1.5, size=12).astype(np.float32)
+    if dtype == "bf16":
+        logits = _bf16_exact(logits)
+    print(f"case peaked/{dtype}", flush=True)
+    for temperature in (0.6, 1.0):
+        got = gpu_draw(logits, temperature, 4321, 9, dev, dtype)
+        compare(f"peaked/{dtype}", logits, temperature, 4321, 9, got)
+
+
 def test_draw_matches_oracle_bf16(dev):
     rng = np.random.default_rng(210)
     logits = _bf16_exact(rng.normal(0, 3, size=(16, VOCAB)))

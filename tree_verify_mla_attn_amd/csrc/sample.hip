@@ -15,9 +15,10 @@
 // less a constant, so token ~ softmax(logit / T).  T = 0: argmax of the logits.  A row
 // whose logits are all -inf yields -1.
 //
-// HBM-bound: one workgroup per row streams the row once; a thread takes 8 consecutive
-// entries per step (one generator block), so every step of the workgroup reads a
-// contiguous 8 KB (fp32) or 4 KB (bf16).
+// One workgroup per row streams the row once; a thread takes 8 consecutive entries per
+// step (one generator block), so every step of the workgroup reads a contiguous 8 KB
+// (fp32) or 4 KB (bf16).  The generator dominates on flat logits; on peaked ones the
+// blocks that cannot hold the winner skip it (exact pruning, below).
 #include "common.h"
 
 namespace kdt {
@@ -83,6 +84,29 @@ __device__ __forceinline__ float mul_sub_rounded(float a, float b, float g) {
   return ab - g;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf,
+                                                             false)));
+}
+
+// Largest value over the wavefront (no NaN).
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// u <= 1 - 2^-24 gives -log2(-log2 u) <= 23.47, so no key exceeds its scaled logit by more
+// than this (plus a relative margin for the rounding of large scaled logits).
+constexpr float KEY_HEADROOM = 24.0f;
+
 // (value, index) of the larger; equal values -> lower index; index -1 = nothing yet.
 __device__ __forceinline__ void keep_best(float& bz, int& bi, float z, int i) {
   if (i < 0) return;
@@ -96,6 +120,7 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SampleParams p) {
   __shared__ float s_z[SAMPLE_THREADS / 64];
   __shared__ int s_i[SAMPLE_THREADS / 64];
+  __shared__ float s_bound;  // a key some lane of the workgroup has reached
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int vocab = p.vocab;
@@ -103,10 +128,35 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
   float bz = -INFINITY;
   int bi = -1;
   const bool greedy = p.temperature == 0.0f;
+  if (tid == 0) s_bound = -INFINITY;
+  __syncthreads();
   const float cs = greedy ? 1.0f : __fdiv_rn(1.4426950408889634f, p.temperature);
-  for (int64_t g = tid; g * 8 < vocab; g += SAMPLE_THREADS) {
+  // Lower bound of the winning key: the largest key the lanes of the workgroup have seen,
+  // shared through one LDS word without synchronisation (every value written is some
+  // lane's key, so a stale or overwritten value is still a lower bound).  A block of 8
+  // entries whose largest scaled logit plus the headroom is below it cannot hold the
+  // winner (its keys are strictly smaller), so its generator block and logarithms are
+  // skipped; the result is unchanged.
+  // The trip count is uniform per wavefront (all lanes take part in the wave maximum);
+  // entries past the vocabulary read as -inf.
+  float wave_best = -INFINITY;
+  const int64_t n_blocks = ((int64_t)vocab + 7) / 8;
+  int step = 0;
+  for (int64_t g = tid; g - (tid & 63) < n_blocks; g += SAMPLE_THREADS, ++step) {
     float x[8];
     load8<BF16, VEC>(row, g * 8, vocab, x);
+    if (!greedy) {
+      if ((step & 7) == 0) {  // a stale bound is still a bound
+        wave_best = fmaxf(wave_max_f(bz), s_bound);
+        if ((tid & 63) == 0 && wave_best > s_bound) s_bound = wave_best;
+      }
+      const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float sm = xm * cs;
+      // skip unless some key of the block could reach the bound (an all -inf block gives
+      // NaN here and is skipped; the bound starts at -inf, which never skips)
+      if (!(sm + KEY_HEADROOM + fabsf(sm) * 0x1p-20f >= fmaxf(bz, wave_best))) continue;
+    }
     if (greedy) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
