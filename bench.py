@@ -12,6 +12,10 @@ Prints ONE JSON line (rank 0):
                PFLOP/s), from HIP events recorded on the launch stream around it in
                every timed step (the call is issued as its two phases for that)
   cpu_baseline = the float64 oracle on a bounded sample of the same workload
+  call_ms_percentiles = per-call event times (p10 / median / p90) and a cold-cache median
+               (an untimed 1 GB write before each of --cold-calls extra calls)
+  measured_peaks = a large bf16 / fp32 GEMM and a 1 GiB copy on the same box, with the
+               attention kernel's fraction of them beside the spec-peak fractions
   greedy_step  = per-launch device time of the draft-tree build, tree packing and greedy
                accept kernels at the workload's tree shape (graph-replayed), beside the
                host heap oracle's build time for the same batch; step_us = the whole
@@ -78,6 +82,10 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--cold-calls", type=int, default=10,
+                    help="extra calls, each after an untimed 1 GB write, for a cold-cache median")
+    ap.add_argument("--no-measure-peaks", dest="measure_peaks", action="store_false",
+                    help="skip the GEMM / copy reference measurements")
     ap.add_argument("--no-greedy-step", action="store_true",
                     help="skip timing the tree build / pack / accept kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -117,6 +125,41 @@ def cpu_baseline(inp, seconds):
             "sample": f"float64 numpy oracle on the first {done} of {inp.batch} requests "
                       f"({flops:.3e} algorithmic FLOPs in {dt:.2f} s, BLAS threads={threads}, "
                       f"host cpus={os.cpu_count()})"}
+
+
+def measured_peaks(torch, dev):
+    """What the box reaches on plain work, beside the spec peaks: a large square GEMM
+    through torch (hipBLASLt; 2-D, contiguous operands) in bf16 and fp32, and a 1 GiB
+    device-to-device copy (bytes read + written per second)."""
+    out = {}
+    n = 8192
+    for name, dt in (("gemm_bf16_TFLOPs", torch.bfloat16), ("gemm_fp32_TFLOPs", torch.float32)):
+        a = torch.randn((n, n), device=dev).to(dt).contiguous()
+        b = torch.randn((n, n), device=dev).to(dt).contiguous()
+        c = torch.matmul(a, b)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10 if dt == torch.bfloat16 else 3
+        e0.record()
+        for _ in range(reps):
+            c = torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        out[name] = round(2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        del a, b, c
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    out["copy_GBs"] = round(2.0 * src.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    return out
 
 
 def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle=True,
@@ -322,9 +365,30 @@ def main():
     if st:
         raise RuntimeError(f"device status {B.decode_status(st)}")
     ms = wall * 1e3 / args.steps
-    call_ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)) / args.steps
+    call_each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    att_each = sorted(mid[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    call_ms = sum(call_each) / args.steps
     pre_ms = sum(ev[i].elapsed_time(mid[i]) for i in range(args.steps)) / args.steps
-    ev_ms = sum(mid[i].elapsed_time(ev[i + 1]) for i in range(args.steps)) / args.steps
+    ev_ms = sum(att_each) / args.steps
+
+    def pct(xs, q):
+        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+    # cold caches: an untimed 1 GB write before each call evicts L2 and the MALL
+    cold = []
+    if args.cold_calls > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(args.cold_calls):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        cold.sort()
+    measured = measured_peaks(torch, dev) if args.measure_peaks else None
 
     dtype = inp.dtype
     value = flops / (ms * 1e-3) / 1e12
@@ -359,9 +423,20 @@ def main():
                 "frac": round(alg_bytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "measured": traffic,
                 "measured_GBs": round(traffic["bytes"] / (ev_ms * 1e-3) / 1e9, 1) if traffic else None},
+        "call_ms_percentiles": {"p10": round(pct(call_each, 0.1), 5),
+                                "median": round(pct(call_each, 0.5), 5),
+                                "p90": round(pct(call_each, 0.9), 5),
+                                "cold_median": round(pct(cold, 0.5), 5) if cold else None,
+                                "cold_calls": len(cold)},
         "kernel_ms": {"attention": round(ev_ms, 5), "prepass": round(pre_ms, 5),
                       "call": round(call_ms, 5)},
     }
+    if measured:
+        res["measured_peaks"] = measured
+        key = "gemm_bf16_TFLOPs" if dtype == "bf16" else "gemm_fp32_TFLOPs"
+        res["roofline"]["frac_of_measured_peak"] = round(achieved / measured[key], 4)
+        res["hbm"]["frac_of_measured_copy"] = round(
+            alg_bytes / (ev_ms * 1e-3) / 1e9 / measured["copy_GBs"], 4)
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
