@@ -86,6 +86,9 @@ def parse():
                     help="extra calls, each after an untimed 1 GB write, for a cold-cache median")
     ap.add_argument("--no-measure-peaks", dest="measure_peaks", action="store_false",
                     help="skip the GEMM / copy reference measurements")
+    ap.add_argument("--sharded-share", action="store_true",
+                    help="also time one GPU's share of the 32768-key workload under 8-way "
+                         "context parallelism (always on with --workload 5)")
     ap.add_argument("--no-greedy-step", action="store_true",
                     help="skip timing the tree build / pack / accept kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -120,11 +123,60 @@ def cpu_baseline(inp, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                         model)
+    except OSError:  # pragma: no cover
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"float64 numpy oracle on the first {done} of {inp.batch} requests "
                       f"({flops:.3e} algorithmic FLOPs in {dt:.2f} s, BLAS threads={threads}, "
-                      f"host cpus={os.cpu_count()})"}
+                      f"host cpus={os.cpu_count()}, affinity={affinity}, cpu={model})"}
+
+
+def sharded_share(B, synth, torch, dev, parts=8, steps=20):
+    """One GPU's share of the 32768-key workload under context parallelism across `parts`
+    GPUs: the same 4 requests and trees, 32768 / parts prefix keys each, giving that GPU's
+    partial output and log-sum-exp (num_splits chosen as for a single GPU); the
+    cross-GPU merge would be the same LSE merge the split path runs."""
+    import numpy as np
+    c = synth.CONFIGS[5]
+    rng, prefix, parents = synth.config_trees(5)
+    share = [int(x) // parts for x in prefix]
+    inp = synth.make_inputs(rng, num_heads=c["heads"], prefix_lens=share, parents=parents,
+                            dtype=c["dtype"])
+    d = synth.device_tensors(inp, dev)
+    splits = B.choose_num_splits(inp.batch, inp.num_heads, inp.max_q_len,
+                                 float(np.mean(share)) + inp.max_q_len)
+    call = B.VerifyAttn()
+    out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)
+    ws_bytes = B.kdtree_verify_attn_workspace_bytes(inp.total_q, inp.total_kv, inp.batch,
+                                                    inp.num_heads, splits, B.KDTREE_DTYPE_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def run():
+        call(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+             d["tree_parent"], d["q_len"], inp.scale, out_lat=out, out_lse=lse,
+             num_splits=splits, max_q_len=inp.max_q_len, workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": f"{c['name']} / {parts}-way context share", "prefix_per_gpu": share[0],
+            "num_splits": splits, "ms": round(ms, 5),
+            "TFLOPs": round(inp.algorithmic_flops() / (ms * 1e-3) / 1e12, 2),
+            "merge_message_MB_per_gpu": round(inp.total_q * inp.num_heads * 513 * 4 / 1e6, 1)}
 
 
 def measured_peaks(torch, dev):
@@ -447,6 +499,8 @@ def main():
               file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if args.workload == 5 or args.sharded_share:
+        res["sharded_share"] = sharded_share(B, synth, torch, dev)
     if not args.no_greedy_step:
         res["greedy_step"] = greedy_step_timing(
             B, synth, torch, dev, args.workload, cpu_oracle=args.cpu_seconds > 0,
