@@ -325,3 +325,35 @@ def test_rows_past_the_packed_total_left_unwritten(dev, splits):
     r_out, r_lse = verify_attn_inputs(inp)
     check(f"spare_rows/{splits}", inp, out[:inp.total_q].double().cpu().numpy(),
           lse[:inp.total_q].double().cpu().numpy(), r_out, r_lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_spare_kv_rows_ignored(dev, dtype):
+    """total_kv larger than the packed total: the spare rows are never read, so filling
+    them with huge values changes nothing."""
+    inp = EDGE["ragged_batch5_h64"](dtype)
+    d = synth.device_tensors(inp, dev)
+    extra = 100
+
+    def pad(t):
+        tail = torch.full((extra,) + tuple(t.shape[1:]), 3.0e4, dtype=t.dtype, device=dev)
+        return torch.cat([t, tail]).contiguous()
+    print(f"case spare_kv/{dtype}", flush=True)
+    ref = B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+                        d["tree_parent"], d["q_len"], inp.scale, max_q_len=65, num_splits=3)
+    got = B.verify_attn(d["q_lat"], d["q_rope"], pad(d["kv_lat"]), pad(d["k_rope"]),
+                        d["prefix_len"], d["tree_parent"], d["q_len"], inp.scale, max_q_len=65,
+                        num_splits=3)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+
+
+def test_large_batch_of_small_requests(dev):
+    """300 requests with 1..9 nodes and prefixes 0..200 (the request ranking, offsets and
+    tile bookkeeping at a batch far above the workloads')."""
+    rng = np.random.default_rng(77)
+    parents = [synth.random_tree(rng, int(rng.integers(1, 10))) for _ in range(300)]
+    prefix = rng.integers(0, 201, size=300)
+    inp = synth.make_inputs(rng, num_heads=8, prefix_lens=prefix, parents=parents, dtype="bf16")
+    full_check("batch300", inp, dev)
+    full_check("batch300", inp, dev, num_splits=2)
