@@ -26,14 +26,51 @@ namespace {
 
 constexpr int SAMPLE_THREADS = 256;
 
+// The 128-bit product a * m as (lo, hi) from four 32 x 32 -> 64 multiply-adds:
+// x = a0 m0, y = a1 m0 + x1, z = a0 m1 + y (65 bits: z + 2^64 c), so that
+// a*m = x0 + 2^32 z0 + 2^64 (a1 m1 + z1 + 2^32 c).  The carry c comes from the
+// multiply-add's own carry-out mask, which saves the zero-extended register pair (two
+// moves) and the add with carry that the compiler builds for an explicit 65-bit sum; a
+// VALU write of a lane mask takes two wait states before a VALU reads it as a select.
+__device__ __forceinline__ void mul_wide(uint64_t a, uint32_t m0, uint32_t m1, uint64_t& lo,
+                                         uint64_t& hi) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint64_t x = (uint64_t)a0 * m0;
+  const uint64_t y = (uint64_t)a1 * m0 + (x >> 32);
+  uint64_t z;
+  uint32_t c;
+  uint64_t cm;
+  asm("v_mad_u64_u32 %0, %1, %3, %4, %5\n\t"
+      "s_nop 1\n\t"
+      "v_cndmask_b32_e64 %2, 0, 1, %1"
+      : "=&v"(z), "=&s"(cm), "=v"(c)
+      : "v"(a0), "s"(m1), "v"(y));
+  hi = (uint64_t)a1 * m1 + (((uint64_t)c << 32) | (z >> 32));
+  lo = (uint32_t)x | (z << 32);
+}
+
+// a ^ b ^ c in one instruction (gfx950 three-input bit operation, truth table 0x96)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+  return r;
+}
+
+__device__ __forceinline__ uint64_t xor3_64(uint64_t a, uint64_t b, uint64_t c) {
+  return (uint64_t)xor3((uint32_t)a, (uint32_t)b, (uint32_t)c) |
+         ((uint64_t)xor3((uint32_t)(a >> 32), (uint32_t)(b >> 32), (uint32_t)(c >> 32)) << 32);
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
-  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint32_t M0L = 0xE14C6C93u, M0H = 0xD2E7470Eu;
+  constexpr uint32_t M1L = 0x95121157u, M1H = 0xCA5A8263u;
   constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    uint64_t lo0, hi0, lo1, hi1;
+    mul_wide(c[0], M0L, M0H, lo0, hi0);
+    mul_wide(c[2], M1L, M1H, lo1, hi1);
+    const uint64_t n0 = xor3_64(hi1, c[1], k0), n2 = xor3_64(hi0, c[3], k1);
     c[0] = n0;
     c[1] = lo1;
     c[2] = n2;
@@ -103,6 +140,20 @@ __device__ __forceinline__ float wave_max_f(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// The uniform of a 32-bit generator word: (2 (x32 >> 9) + 1) 2^-24, formed as
+// (1 + (x32 >> 9) 2^-23) - (1 - 2^-24), where the first operand is the bits
+// 0x3f800000 | (x32 >> 9) and the subtraction is exact (Sterbenz).
+__device__ __forceinline__ float uniform_of(unsigned x32) {
+  return __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, x32, 9)) - 0x1.fffffep-1f;
+}
+
+// log2(-log2(u)) with the hardware base-2 log: within an ulp relative to the exact value
+// over all u here, also near 1, where the small -log2(u) decide the argmax (u >= 2^-24
+// and -log2(u) >= 2^-24 / ln 2 are normal numbers).  It falls as u rises.
+__device__ __forceinline__ float gumbel_log2(float u) {
+  return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+}
+
 // u <= 1 - 2^-24 gives -log2(-log2 u) <= 23.47, so no key exceeds its scaled logit by more
 // than this (plus a relative margin for the rounding of large scaled logits).
 constexpr float KEY_HEADROOM = 24.0f;
@@ -136,7 +187,8 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
   // lane's key, so a stale or overwritten value is still a lower bound).  A block of 8
   // entries whose largest scaled logit plus the headroom is below it cannot hold the
   // winner (its keys are strictly smaller), so its generator block and logarithms are
-  // skipped; the result is unchanged.
+  // skipped.  A second test after the generator, with the block's largest uniform, skips
+  // the logarithms of most blocks that pass the first.  Neither changes the result.
   // The trip count is uniform per wavefront (all lanes take part in the wave maximum);
   // entries past the vocabulary read as -inf.
   float wave_best = -INFINITY;
@@ -145,18 +197,6 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
   for (int64_t g = tid; g - (tid & 63) < n_blocks; g += SAMPLE_THREADS, ++step) {
     float x[8];
     load8<BF16, VEC>(row, g * 8, vocab, x);
-    if (!greedy) {
-      if ((step & 7) == 0) {  // a stale bound is still a bound
-        wave_best = fmaxf(wave_max_f(bz), s_bound);
-        if ((tid & 63) == 0 && wave_best > s_bound) s_bound = wave_best;
-      }
-      const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      const float sm = xm * cs;
-      // skip unless some key of the block could reach the bound (an all -inf block gives
-      // NaN here and is skipped; the bound starts at -inf, which never skips)
-      if (!(sm + KEY_HEADROOM + fabsf(sm) * 0x1p-20f >= fmaxf(bz, wave_best))) continue;
-    }
     if (greedy) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -166,17 +206,33 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
         }
       continue;
     }
+    if ((step & 7) == 0) {  // a stale bound is still a bound
+      wave_best = fmaxf(wave_max_f(bz), s_bound);
+      if ((tid & 63) == 0 && wave_best > s_bound) s_bound = wave_best;
+    }
+    const float best = fmaxf(bz, wave_best);
+    const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float sm = xm * cs;
+    // skip unless some key of the block could reach the bound (an all -inf block gives
+    // NaN here and is skipped; the bound starts at -inf, which never skips)
+    if (!(sm + KEY_HEADROOM + fabsf(sm) * 0x1p-20f >= best)) continue;
     uint64_t c[4] = {(uint64_t)g, (uint64_t)r, 0ull, 0ull};
     philox4x64_10(c, p.seed, p.offset);
+    unsigned w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = (unsigned)(c[k >> 1] >> (32 * (k & 1)));
+    // Second test, with the block's own uniforms: u rises with its word and a key falls
+    // with gumbel_log2(u), so no key of the block exceeds sm - gumbel_log2(u of the
+    // largest word).  The margin covers the logarithms' error (about an ulp each, at most
+    // ~2e-7 absolute through the outer one) and the rounding of the products.
+    const unsigned wmax = max(max(max(w[0], w[1]), max(w[2], w[3])),
+                              max(max(w[4], w[5]), max(w[6], w[7])));
+    const float gmin = gumbel_log2(uniform_of(wmax));
+    if (!(sm - gmin + (fabsf(sm) + fabsf(gmin)) * 0x1p-20f + 0x1p-20f >= best)) continue;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const unsigned x32 = (unsigned)(c[k >> 1] >> (32 * (k & 1)));
-      const float u = (float)((x32 >> 9) * 2u + 1u) * 0x1p-24f;
-      // the hardware base-2 log: within an ulp relative to the exact value over all u
-      // here, also near 1, where the small -log2(u) decide the argmax (u >= 2^-24 and
-      // -log2(u) >= 2^-24 / ln 2 are normal numbers)
-      const float gum = __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
-      const float z = mul_sub_rounded(x[k], cs, gum);
+      const float z = mul_sub_rounded(x[k], cs, gumbel_log2(uniform_of(w[k])));
       if (z > bz) {
         bz = z;
         bi = (int)(g * 8 + k);
