@@ -348,12 +348,25 @@ def test_spare_kv_rows_ignored(dev, dtype):
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
 
 
-def test_large_batch_of_small_requests(dev):
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_large_batch_of_small_requests(dev, dtype):
     """300 requests with 1..9 nodes and prefixes 0..200 (the request ranking, offsets and
     tile bookkeeping at a batch far above the workloads')."""
     rng = np.random.default_rng(77)
     parents = [synth.random_tree(rng, int(rng.integers(1, 10))) for _ in range(300)]
     prefix = rng.integers(0, 201, size=300)
-    inp = synth.make_inputs(rng, num_heads=8, prefix_lens=prefix, parents=parents, dtype="bf16")
-    full_check("batch300", inp, dev)
-    full_check("batch300", inp, dev, num_splits=2)
+    inp = synth.make_inputs(rng, num_heads=8, prefix_lens=prefix, parents=parents, dtype=dtype)
+    full_check(f"batch300/{dtype}", inp, dev)
+    full_check(f"batch300/{dtype}", inp, dev, num_splits=2)
+
+
+def test_batch_beyond_the_ranking_limit(dev):
+    """4100 requests, more than the pre-pass ranks (4096): the work is then handed out in
+    request order, and each workgroup sums the lengths of up to 4099 earlier requests."""
+    rng = np.random.default_rng(78)
+    n = 4100
+    parents = [synth.random_tree(rng, int(rng.integers(1, 4))) for _ in range(n)]
+    prefix = rng.integers(0, 40, size=n)
+    inp = synth.make_inputs(rng, num_heads=2, prefix_lens=prefix, parents=parents, dtype="bf16")
+    full_check("batch4100", inp, dev)
+    full_check("batch4100", inp, dev, num_splits=3)
