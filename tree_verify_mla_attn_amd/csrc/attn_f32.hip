@@ -66,11 +66,19 @@ __device__ __forceinline__ f32x4 qk_tile(const float4 (&qf)[36], int lane) {
 #pragma unroll
   for (int kb = 0; kb < 36; ++kb) {
     const float4 a = *(const float4*)(kt + key * KSTRIDE + 16 * kb + 4 * g);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, qf[kb].x, s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, qf[kb].y, s1, 0, 0, 0);
-    s2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, qf[kb].z, s2, 0, 0, 0);
-    s3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, qf[kb].w, s3, 0, 0, 0);
+    // Q is an AGPR operand of these MFMAs, so the register allocator keeps all 144 Q
+    // values in the AGPR file for the whole loop.  Q and O together (272 values) exceed
+    // the 256 VGPRs; with Q in VGPRs, O moved between the two files every tile.
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %4, %8, %0\n\t"
+                 "v_mfma_f32_16x16x4_f32 %1, %5, %9, %1\n\t"
+                 "v_mfma_f32_16x16x4_f32 %2, %6, %10, %2\n\t"
+                 "v_mfma_f32_16x16x4_f32 %3, %7, %11, %3"
+                 : "+v"(s0), "+v"(s1), "+v"(s2), "+v"(s3)
+                 : "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w),
+                   "a"(qf[kb].x), "a"(qf[kb].y), "a"(qf[kb].z), "a"(qf[kb].w));
   }
+  // wait states between the last MFMAs and VALU reads of their results
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
   return (s0 + s1) + (s2 + s3);
 }
 
