@@ -38,14 +38,14 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 
+# the sources of the kernel whose HBM counters are stored (the bf16 attention kernel)
 KERNEL_SOURCES = ("tree_verify_mla_attn_amd/csrc/attn_bf16.hip",
-                  "tree_verify_mla_attn_amd/csrc/attn_f32.hip",
                   "tree_verify_mla_attn_amd/csrc/common.h")
 
 
 def kernel_source_digest():
-    """sha256 over the attention kernels' sources: stored HBM counter readings are used
-    only while it still matches the digest recorded with them."""
+    """sha256 over the bf16 attention kernel's sources: stored HBM counter readings are
+    used only while it still matches the digest recorded with them."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
