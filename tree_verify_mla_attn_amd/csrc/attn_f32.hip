@@ -7,8 +7,8 @@
 //   S^T = K Q^T  (16 keys x 16 rows per wave; each lane holds one query row),
 //   online softmax in the log2 domain with a lazy rescale,
 //   O^T += V^T P^T with V read straight from the fp32 tile (V = latent part of K).
-// The tile is staged through a padded, double-buffered LDS layout; the next tile's
-// global loads are in flight in VGPRs while the current tile is processed.
+// The tiles arrive by 16-byte global->LDS DMA into two LDS stages: the next tile's copy is
+// in flight while the current tile is processed, and no VGPR stages it.
 #include "common.h"
 
 namespace kdt {
@@ -17,47 +17,66 @@ namespace {
 constexpr int BM = 64;
 constexpr int BN = 16;
 constexpr int NTHR = 256;
-constexpr int KSTRIDE = DK + 4;  // floats per LDS key row (pad: conflict-free reads)
 constexpr float RESCALE_THRESHOLD = 8.0f;
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-__shared__ __attribute__((aligned(16))) float sK0[BN * KSTRIDE];
-__shared__ __attribute__((aligned(16))) float sK1[BN * KSTRIDE];
+#define LDS_AS __attribute__((address_space(3)))
+
+// LDS stage (floats): latent rows [16 keys][512 + 4 pad] (a 2064-byte stride, so each row
+// is two contiguous 1 KB copies and a row's 16-byte chunk c sits in bank group
+// (key + c) mod 16), then rope rows [16 keys][64] whose chunk c of key k sits at slot
+// c ^ k.  Score reads (16 keys, one chunk), value reads (4 keys x 16 consecutive floats)
+// and rope reads are all bank-conflict free.
+constexpr int LSTRIDE = DL + 4;
+constexpr int STAGE_LAT = BN * LSTRIDE;
+constexpr int STAGE_FLOATS = STAGE_LAT + BN * DR;
+// Separate objects per stage: the compiler's wait-count insertion can then tell that a
+// copy into one stage does not alias reads of the other.
+__shared__ __attribute__((aligned(1024))) float sK0[STAGE_FLOATS];
+__shared__ __attribute__((aligned(1024))) float sK1[STAGE_FLOATS];
 __shared__ int32_t sParent32[MAX_QLEN];
 __shared__ int64_t sRed32[8];
 __shared__ int32_t sFlag32;
 
 template <int STAGE> __device__ __forceinline__ float* ktile() { return STAGE ? sK1 : sK0; }
 
-// Each thread moves 9 of the tile's 16 x 144 float4 chunks (latent chunks 0..127, rope
-// chunks 128..143 of every key).
-__device__ __forceinline__ void load_tile(float4 (&r)[9], const float* kv_lat, const float* k_rope,
-                                          int64_t kv_row0, int key0, int key_last, int tid) {
-#pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int item = tid + NTHR * i;
-    const int key = item / 144, c = item % 144;
-    const int64_t k = kv_row0 + min(key0 + key, key_last);
-    r[i] = c < 128 ? *(const float4*)(kv_lat + k * DL + c * 4)
-                   : *(const float4*)(k_rope + k * DR + (c - 128) * 4);
-  }
+// 16-byte global -> LDS copies (64 lanes fill 1 KB at `lds`) through a buffer descriptor
+// on a wave-uniform base; lane and row offsets stay below 32 KB.
+__device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& rsrc, float* lds,
+                                      unsigned lane_off, unsigned row_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)lds, 16, (int)lane_off,
+                                           (int)row_off, 0, 0);
 }
 
+// Copy tile keys [key0, key0 + 16) (clamped to key_last; both relative to the request's
+// first row) into stage STAGE.  Wave w moves latent rows 4w..4w+3 (two 1 KB halves each)
+// and rope rows 4w..4w+3 (one instruction): nine copies per wave.
 template <int STAGE>
-__device__ __forceinline__ void store_tile(const float4 (&r)[9], int tid) {
+__device__ __forceinline__ void issue_tile(const float* kv_lat_req, const float* k_rope_req,
+                                           int key0, int key_last, int wave, int lane) {
   float* kt = ktile<STAGE>();
+  const __amdgpu_buffer_rsrc_t lat = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kv_lat_req + (int64_t)key0 * DL), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rope = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k_rope_req + (int64_t)key0 * DR), (short)0, -1, 0x00020000);
+  const int last = key_last - key0;  // >= 0
 #pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int item = tid + NTHR * i;
-    const int key = item / 144, c = item % 144;
-    *(float4*)(kt + key * KSTRIDE + c * 4) = r[i];
+  for (int n = 0; n < 8; ++n) {
+    const int row = wave * 4 + (n >> 1), half = n & 1;
+    const int src = min(row, last);
+    dma16(lat, kt + row * LSTRIDE + half * 256, (unsigned)lane * 16u,
+          (unsigned)(src * DL * 4 + half * 1024));
   }
+  const int row = wave * 4 + (lane >> 4), slot = lane & 15;
+  dma16(rope, kt + STAGE_LAT + wave * 4 * DR,
+        (unsigned)(min(row, last) * DR * 4 + ((slot ^ row) & 15) * 16), 0u);
 }
 
 template <int STAGE>
 __device__ __forceinline__ f32x4 qk_tile(const float4 (&qf)[36], int lane) {
   const float* kt = ktile<STAGE>();
+  const float* kr = kt + STAGE_LAT;
   const int key = lane & 15, g = lane >> 4;
   // Four independent accumulation chains (one per float of the 16-byte operand), summed
   // pairwise at the end: each chain adds 144 products, which keeps the fp32 rounding of
@@ -65,7 +84,8 @@ __device__ __forceinline__ f32x4 qk_tile(const float4 (&qf)[36], int lane) {
   f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};
 #pragma unroll
   for (int kb = 0; kb < 36; ++kb) {
-    const float4 a = *(const float4*)(kt + key * KSTRIDE + 16 * kb + 4 * g);
+    const float4 a = kb < 32 ? *(const float4*)(kt + key * LSTRIDE + 16 * kb + 4 * g)
+                             : *(const float4*)(kr + key * DR + (((kb - 32) * 4 + g) ^ key) * 4);
     // Q is an AGPR operand of these MFMAs, so the register allocator keeps all 144 Q
     // values in the AGPR file for the whole loop.  Q and O together (272 values) exceed
     // the 256 VGPRs; with Q in VGPRs, O moved between the two files every tile.
@@ -90,7 +110,7 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[32], const f32x4& pr, int lan
   for (int fb = 0; fb < 32; ++fb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float a = kt[(4 * g + r) * KSTRIDE + fb * 16 + fl];
+      const float a = kt[(4 * g + r) * LSTRIDE + fb * 16 + fl];
       o[fb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, pr[r], o[fb], 0, 0, 0);
     }
   }
@@ -261,30 +281,33 @@ void verify_attn_f32_kernel(VerifyParams p) {
   for (int fb = 0; fb < 32; ++fb) o[fb] = f32x4{};
   RowState32 st{-INFINITY, 0.0f};
 
-  float4 pre[9];
-  load_tile(pre, kv_lat, k_rope, kvoff, k_begin, key_last, tid);
-  store_tile<0>(pre, tid);
+  // Tile j sits in stage j % 2; the copy of tile j+1 into the other stage (read by tile
+  // j-1 before the previous barrier) is in flight while tile j is processed.
+  const float* kv_lat_req = kv_lat + kvoff * DL;
+  const float* k_rope_req = k_rope + kvoff * DR;
+  issue_tile<0>(kv_lat_req, k_rope_req, k_begin, key_last, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int j = 0; j < n_tiles; j += 2) {
     {
       const int key0 = k_begin + j * BN;
-      if (j + 1 < n_tiles) load_tile(pre, kv_lat, k_rope, kvoff, key0 + BN, key_last, tid);
+      if (j + 1 < n_tiles) issue_tile<1>(kv_lat_req, k_rope_req, key0 + BN, key_last, wave, lane);
       f32x4 s = qk_tile<0>(qf, lane);
       softmax_tile(s, o, st, c, key0 + BN > mask_from, key0, k_end, P, node, anc, lane);
       pv_tile<0>(o, s, lane);
       if (j + 1 >= n_tiles) break;
-      store_tile<1>(pre, tid);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
     {
       const int key0 = k_begin + (j + 1) * BN;
-      if (j + 2 < n_tiles) load_tile(pre, kv_lat, k_rope, kvoff, key0 + BN, key_last, tid);
+      if (j + 2 < n_tiles) issue_tile<0>(kv_lat_req, k_rope_req, key0 + BN, key_last, wave, lane);
       f32x4 s = qk_tile<1>(qf, lane);
       softmax_tile(s, o, st, c, key0 + BN > mask_from, key0, k_end, P, node, anc, lane);
       pv_tile<1>(o, s, lane);
       if (j + 2 >= n_tiles) break;
-      store_tile<0>(pre, tid);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
