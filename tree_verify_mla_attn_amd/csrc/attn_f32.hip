@@ -3,7 +3,8 @@
 // Same operation as the bf16 kernel ("The Milestone Commit: Cementing Phase 1 ...",
 // section "The Context", item 2), computed with fp32 MFMA (v_mfma_f32_16x16x4_f32) so
 // that products and sums stay in fp32.  One workgroup = 4 waves = 64 query rows; each
-// wave owns 16 rows with its Q fragment (16 x 576 fp32) in VGPRs.  Per 16-key tile:
+// wave owns 16 rows with its Q fragment (16 x 576 fp32) in AGPRs, as the B operand of the
+// score MFMAs, which leaves the VGPRs to the 512-wide O accumulator.  Per 16-key tile:
 //   S^T = K Q^T  (16 keys x 16 rows per wave; each lane holds one query row),
 //   online softmax in the log2 domain with a lazy rescale,
 //   O^T += V^T P^T with V read straight from the fp32 tile (V = latent part of K).
