@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, help="1..5 (default: batch-64 ragged)")
     ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--split-ratio", type=float, default=None,
+                    help="split-KV chunk ratio (1 = equal; default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--cold-calls", type=int, default=10,
@@ -321,14 +323,15 @@ def greedy_step_timing(B, synth, torch, dev, cfg, reps=64, replays=5, cpu_oracle
         # the whole step on the device: build -> pack -> verify attention over the built
         # trees (the workload's q / kv rows, which its trees fill exactly) -> accept on
         # fixed target tokens (the target model's argmax is outside this path)
-        vq, vqr, vkv, vkr, vprefix, vout, vlse, vws, vsplits, vscale = verify
+        vq, vqr, vkv, vkr, vprefix, vout, vlse, vws, vsplits, vscale, vratio = verify
         if int(vq.shape[0]) != batch * width:
             res["step_us"] = None
         else:
             def chain(s):
                 assert build(s) == 0 and pack(s) == 0
                 B.VerifyAttn()(vq, vqr, vkv, vkr, vprefix, pk_par, o_q, vscale, out_lat=vout,
-                               out_lse=vlse, num_splits=vsplits, max_q_len=width, workspace=vws)
+                               out_lse=vlse, num_splits=vsplits, max_q_len=width, workspace=vws,
+                               split_ratio=vratio)
                 assert accept(s) == 0
             cs = torch.cuda.Stream(device=dev)
             cs.wait_stream(torch.cuda.current_stream(dev))
@@ -375,6 +378,7 @@ def main():
     dev = torch.device("cuda:0")
     inp = synth.config_inputs(args.workload)
     splits = args.num_splits or inp.num_splits
+    ratio = args.split_ratio if args.split_ratio is not None else inp.split_ratio
     d = synth.device_tensors(inp, dev)
     flops = inp.algorithmic_flops()
     alg_bytes = inp.algorithmic_bytes()
@@ -391,7 +395,7 @@ def main():
 
     def step(mid=None):
         call(*argv, out_lat=out, out_lse=lse, num_splits=splits, max_q_len=inp.max_q_len,
-             workspace=ws, status=status, mid_event=mid)
+             workspace=ws, status=status, mid_event=mid, split_ratio=ratio)
 
     for _ in range(args.warmup):
         step()
@@ -464,7 +468,7 @@ def main():
         "data": "synthetic (seeded N(0,1) MLA tensors, best-first draft trees)",
         "config": {"workload": inp.name, "batch": inp.batch, "heads": inp.num_heads,
                    "q_len": int(inp.max_q_len), "total_q": inp.total_q, "total_kv": inp.total_kv,
-                   "num_splits": splits, "d_latent": 512, "d_rope": 64,
+                   "num_splits": splits, "split_ratio": ratio, "d_latent": 512, "d_rope": 64,
                    "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
         "roofline": {"bound": "mfma", "kernel": "attention" + (" + merge" if splits > 1 else ""),
                      "achieved": round(achieved, 3), "peak": peak,
@@ -505,7 +509,7 @@ def main():
         res["greedy_step"] = greedy_step_timing(
             B, synth, torch, dev, args.workload, cpu_oracle=args.cpu_seconds > 0,
             verify=(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], out, lse,
-                    ws, splits, inp.scale))
+                    ws, splits, inp.scale, ratio))
     print(json.dumps(res), flush=True)
 
 

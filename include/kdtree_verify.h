@@ -67,8 +67,9 @@ extern "C" {
                                        total_kv < total_q, or a size overflows */
 #define KDTREE_ERR_QLEN (-3)        /* max_q_len outside [1, KDTREE_MAX_QLEN] */
 #define KDTREE_ERR_DTYPE (-4)       /* dtype not FP32 / BF16 */
-#define KDTREE_ERR_SPLITS (-5)      /* num_splits < 1 or > 256, or workspace NULL /
-                                       smaller than kdtree_verify_attn_workspace_bytes */
+#define KDTREE_ERR_SPLITS (-5)      /* num_splits < 1 or > 256, split_ratio outside (0, 1],
+                                       or workspace NULL / smaller than
+                                       kdtree_verify_attn_workspace_bytes */
 #define KDTREE_ERR_SCALE (-6)       /* scale not finite */
 #define KDTREE_ERR_LAUNCH (-7)      /* HIP launch failure */
 
@@ -114,11 +115,18 @@ size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int
  *                a request whose packed offsets exceed them is skipped and flagged.
  *   dtype        KDTREE_DTYPE_FP32 or KDTREE_DTYPE_BF16 (all four inputs).
  *   num_splits   split-KV factor (1..256).  With S > 1 each request's prefix is cut
- *                into S chunks of ceil(P/S) keys rounded up to a multiple of 32 (the
- *                tail goes with the last chunk; trailing chunks may be empty);
- *                each chunk's partial output + lse is written to `workspace` and a
- *                merge pass combines them ("The Milestone Commit ...", section "What
- *                to defer": flash partial outputs merged for long prefixes).
+ *                into S chunks of whole 32-key tiles (the tail goes with the last
+ *                chunk; chunks may be empty); each chunk's partial output + lse is
+ *                written to `workspace` and a merge pass combines them ("The Milestone
+ *                Commit ...", section "What to defer": flash partial outputs merged for
+ *                long prefixes).
+ *   split_ratio  chunk sizes, in (0, 1].  1: S equal chunks of ceil(P/S) keys rounded
+ *                up to a multiple of 32.  r < 1: geometric chunks, chunk s holding about
+ *                r^s (1 - r) / (1 - r^S) of the prefix (boundaries rounded up to whole
+ *                tiles), and the work is handed out largest chunks first, so that a
+ *                launch whose workgroups overrun a whole number of rounds over the CUs
+ *                ends on small pieces.  The result is the same up to rounding; with
+ *                S = 1 the ratio has no effect.
  *   workspace    device buffer of at least kdtree_verify_attn_workspace_bytes(...)
  *                bytes (may be NULL when that is 0: fp32 inputs with num_splits == 1).
  *                Its contents are scratch; calls sharing a workspace must not overlap.
@@ -135,7 +143,8 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
                            float* out_lat, float* out_lse, void* stream, int32_t batch,
                            int32_t num_heads, int32_t max_q_len, int64_t total_q,
                            int64_t total_kv, int32_t dtype, int32_t num_splits,
-                           void* workspace, size_t workspace_bytes, int32_t* status);
+                           float split_ratio, void* workspace, size_t workspace_bytes,
+                           int32_t* status);
 
 /*
  * The same call in two phases, for callers that time or schedule them apart.  Both
@@ -159,8 +168,8 @@ int32_t kdtree_verify_attn_prepare(const void* q_lat, const void* q_rope, const 
                                    float scale, float* out_lat, float* out_lse, void* stream,
                                    int32_t batch, int32_t num_heads, int32_t max_q_len,
                                    int64_t total_q, int64_t total_kv, int32_t dtype,
-                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                   int32_t* status);
+                                   int32_t num_splits, float split_ratio, void* workspace,
+                                   size_t workspace_bytes, int32_t* status);
 
 int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const void* kv_lat,
                                   const void* k_rope, const int32_t* prefix_len,
@@ -168,8 +177,8 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
                                   float scale, float* out_lat, float* out_lse, void* stream,
                                   int32_t batch, int32_t num_heads, int32_t max_q_len,
                                   int64_t total_q, int64_t total_kv, int32_t dtype,
-                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                  int32_t* status);
+                                  int32_t num_splits, float split_ratio, void* workspace,
+                                  size_t workspace_bytes, int32_t* status);
 
 /* ------------------------------------------------------------------------------------
  * The steps on either side of verify attention in one greedy DDTree step.

@@ -89,6 +89,8 @@ def test_null_pointer_rejected(entry, field):
     (dict(num_splits=300), -5), (dict(num_splits=4), -5), (dict(dtype=1, num_splits=1), -5),
     (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), -5),
     (dict(scale=float("nan")), -6), (dict(scale=float("inf")), -6),
+    (dict(split_ratio=0.0), -5), (dict(split_ratio=-0.5), -5), (dict(split_ratio=1.5), -5),
+    (dict(split_ratio=float("nan")), -5),
 ])
 @pytest.mark.parametrize("entry", ENTRIES)
 def test_bad_arguments_rejected(entry, kw, code):

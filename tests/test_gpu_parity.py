@@ -27,12 +27,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run(inp, dev, num_splits=1, max_q_len=None):
+def run(inp, dev, num_splits=1, max_q_len=None, split_ratio=1.0):
     d = synth.device_tensors(inp, dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     out, lse = B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
                              d["tree_parent"], d["q_len"], inp.scale, num_splits=num_splits,
-                             max_q_len=max_q_len or inp.max_q_len, status=status)
+                             max_q_len=max_q_len or inp.max_q_len, status=status,
+                             split_ratio=split_ratio)
     torch.cuda.synchronize(dev)
     return out, lse, int(status.item())
 
@@ -59,9 +60,9 @@ def check(name, inp, g_out, g_lse, r_out, r_lse):
         assert not (e_lse > BF16_ATOL + BF16_RTOL * np.abs(r_lse)).any(), name
 
 
-def full_check(name, inp, dev, num_splits=1):
-    print(f"case {name} splits={num_splits}", flush=True)
-    out, lse, st = run(inp, dev, num_splits)
+def full_check(name, inp, dev, num_splits=1, split_ratio=1.0):
+    print(f"case {name} splits={num_splits} ratio={split_ratio}", flush=True)
+    out, lse, st = run(inp, dev, num_splits, split_ratio=split_ratio)
     assert st == 0, B.decode_status(st)
     r_out, r_lse = verify_attn_inputs(inp)
     check(name, inp, out.double().cpu().numpy(), lse.double().cpu().numpy(), r_out, r_lse)
@@ -102,12 +103,15 @@ def test_edge_cases(dev, case, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("splits", [2, 3, 16])
-def test_split_kv(dev, splits, dtype):
+@pytest.mark.parametrize("splits,ratio", [(2, 1.0), (3, 1.0), (16, 1.0), (2, 0.45), (3, 0.5),
+                                          (16, 0.7), (5, 0.05)])
+def test_split_kv(dev, splits, ratio, dtype):
+    """Equal splits, and geometric ones (ratio < 1: largest first, boundaries rounded up
+    to whole tiles, so several splits of a short prefix may be empty)."""
     inp = EDGE["ragged_batch5_h64"](dtype)
-    full_check(f"ragged_batch5/{dtype}", inp, dev, num_splits=splits)
+    full_check(f"ragged_batch5/{dtype}", inp, dev, num_splits=splits, split_ratio=ratio)
     inp = EDGE["deep15_p100_h8"](dtype)
-    full_check(f"deep15/{dtype}", inp, dev, num_splits=splits)
+    full_check(f"deep15/{dtype}", inp, dev, num_splits=splits, split_ratio=ratio)
 
 
 def test_bf16_best_first_trees_several_tiles(dev):
@@ -125,7 +129,8 @@ def test_small_workloads_full(dev, cfg):
     """Every element, unsplit and in the benchmark's launch configuration."""
     inp = synth.config_inputs(cfg)
     full_check(f"workload{cfg}", inp, dev)
-    full_check(f"workload{cfg}", inp, dev, num_splits=inp.num_splits)
+    full_check(f"workload{cfg}", inp, dev, num_splits=inp.num_splits,
+               split_ratio=inp.split_ratio)
 
 
 def _sample_rows(inp, rng, per_request_nodes=3, heads=(0, 63)):
@@ -144,8 +149,8 @@ def _sample_rows(inp, rng, per_request_nodes=3, heads=(0, 63)):
 def test_large_workloads_sampled(dev, cfg):
     inp = synth.config_inputs(cfg)
     splits = inp.num_splits
-    print(f"case workload{cfg} splits={splits}", flush=True)
-    out, lse, st = run(inp, dev, splits)
+    print(f"case workload{cfg} splits={splits} ratio={inp.split_ratio}", flush=True)
+    out, lse, st = run(inp, dev, splits, split_ratio=inp.split_ratio)
     assert st == 0, B.decode_status(st)
     out_np = out.cpu().numpy()
     lse_np = lse.cpu().numpy()

@@ -62,7 +62,7 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = i32
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
-                       i32, i32, i32, i64, i64, i32, i32, vp, sz, vp]
+                       i32, i32, i32, i64, i64, i32, i32, ctypes.c_float, vp, sz, vp]
     lib.kdtree_build_ddtree.restype = i32
     lib.kdtree_build_ddtree.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                         vp, vp]
@@ -90,11 +90,13 @@ def kdtree_verify_attn_workspace_bytes(total_q: int, total_kv: int, batch: int, 
 
 def _raw(name, q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale, out_lat,
          out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv, dtype, num_splits,
-         workspace, workspace_bytes, status) -> int:
+         workspace, workspace_bytes, status, split_ratio=1.0) -> int:
+    # split_ratio is last here (keyword, default 1: equal splits); in the C signature it
+    # follows num_splits
     return int(getattr(load_library(), name)(
         q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, ctypes.c_float(scale),
         out_lat, out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv, dtype,
-        num_splits, workspace, workspace_bytes, status))
+        num_splits, ctypes.c_float(split_ratio), workspace, workspace_bytes, status))
 
 
 def kdtree_verify_attn(*args, **kw) -> int:
@@ -306,11 +308,12 @@ class VerifyAttn:
     def __call__(self, q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
                  out_lat=None, out_lse=None, num_splits: int = 1,
                  max_q_len: int = KDTREE_MAX_QLEN, workspace=None, status=None,
-                 phase: str = "all", mid_event=None):
+                 phase: str = "all", mid_event=None, split_ratio: float = 1.0):
         """phase: "all" (kdtree_verify_attn), "prepare" or "attend" (the two halves; an
         "attend" call needs the `workspace` of a "prepare" call on the same inputs).
         mid_event: with phase "all", a torch.cuda.Event recorded on the stream between
-        the two halves (the halves are then issued as two calls)."""
+        the two halves (the halves are then issued as two calls).
+        split_ratio: 1 = equal split-KV chunks; r < 1 = geometric chunks, largest first."""
         import torch
         dtype = q_lat.dtype
         if dtype not in (torch.float32, torch.bfloat16):
@@ -365,7 +368,7 @@ class VerifyAttn:
         for i, name in enumerate(names):
             if i == 1:
                 mid_event.record(torch_stream)
-            rc = _raw(name, *args)
+            rc = _raw(name, *args, split_ratio=float(split_ratio))
             if rc != 0:
                 raise RuntimeError(f"{name} failed: {rc} ({ERRORS.get(rc, '?')})")
         return out_lat, out_lse
@@ -373,8 +376,8 @@ class VerifyAttn:
 
 def verify_attn(*args, **kwargs):
     """verify_attn(q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale,
-    out_lat=None, out_lse=None, num_splits=1, max_q_len=65, workspace=None, status=None)
-    -> (out_lat [total_q, H, 512] fp32, out_lse [total_q, H] fp32)."""
+    out_lat=None, out_lse=None, num_splits=1, max_q_len=65, workspace=None, status=None,
+    split_ratio=1.0) -> (out_lat [total_q, H, 512] fp32, out_lse [total_q, H] fp32)."""
     return VerifyAttn()(*args, **kwargs)
 
 

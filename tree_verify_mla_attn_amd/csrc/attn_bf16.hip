@@ -476,8 +476,11 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const int grank = NUM_XCD * round + ((round & 1) ? NUM_XCD - 1 - xcd : xcd);
   if (grank >= p.batch * p.num_splits) return;
   const int mt = slot % p.m_tiles;
-  const int rank = grank / p.num_splits;
-  const int split = grank % p.num_splits;
+  // Equal splits: requests longest first, then their splits.  Geometric splits: every
+  // request's split 0 (the largest) first, then every split 1, ...
+  const bool geo = p.split_ratio < 1.0f;
+  const int rank = geo ? grank % p.batch : grank / p.num_splits;
+  const int split = geo ? grank / p.batch : grank % p.num_splits;
   int b = p.order ? p.order[rank] : rank;
   if (b < 0 || b >= p.batch) b = rank;
   b = __builtin_amdgcn_readfirstlane(b);
@@ -557,13 +560,9 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
 
   // ---- key range of this split ---------------------------------------------------
   const int S = p.num_splits;
-  int k_begin, k_end;
-  {
-    // chunks of whole 32-key tiles, so every split starts on a V^T tile boundary
-    const int chunk = ((P + S - 1) / S + BN - 1) / BN * BN;
-    k_begin = min(P, split * chunk);
-    k_end = (split == S - 1) ? P + T : min(P, (split + 1) * chunk);
-  }
+  // whole 32-key tiles, so every split starts on a V^T tile boundary
+  int k_begin = split_begin(P, S, p.split_ratio, split);
+  const int k_end = (split == S - 1) ? P + T : split_begin(P, S, p.split_ratio, split + 1);
   const int64_t grow = qoff * H + crow;  // global query row
   if (k_end <= k_begin) {
     // empty split: partial = (0, -inf)

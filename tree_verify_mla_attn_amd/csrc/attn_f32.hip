@@ -171,11 +171,14 @@ void verify_attn_f32_kernel(VerifyParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
 
+  // Row tiles fastest; then request-major for equal splits, split-major (every request's
+  // largest split first) for geometric ones.
   int bid = blockIdx.x;
   const int mt = bid % p.m_tiles;
   bid /= p.m_tiles;
-  const int split = bid % p.num_splits;
-  const int b = bid / p.num_splits;
+  const bool geo = p.split_ratio < 1.0f;
+  const int split = geo ? bid / p.batch : bid % p.num_splits;
+  const int b = geo ? bid % p.batch : bid / p.num_splits;
 
   int64_t qoff = 0, kvoff = 0;
   int bad = 0;
@@ -243,12 +246,8 @@ void verify_attn_f32_kernel(VerifyParams p) {
   }
 
   const int S = p.num_splits;
-  int k_begin, k_end;
-  {
-    const int chunk = ((P + S - 1) / S + 31) / 32 * 32;  // whole 32-key tiles, as the bf16 path
-    k_begin = min(P, split * chunk);
-    k_end = (split == S - 1) ? P + T : min(P, (split + 1) * chunk);
-  }
+  const int k_begin = split_begin(P, S, p.split_ratio, split);
+  const int k_end = (split == S - 1) ? P + T : split_begin(P, S, p.split_ratio, split + 1);
   const int64_t grow = qoff * H + crow;
   if (k_end <= k_begin) {
     if (row_ok) {

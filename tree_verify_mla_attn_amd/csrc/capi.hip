@@ -43,8 +43,8 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
               const int32_t* prefix_len, const int32_t* tree_parent, const int32_t* q_len,
               float scale, float* out_lat, float* out_lse, int32_t batch, int32_t num_heads,
               int32_t max_q_len, int64_t total_q, int64_t total_kv, int32_t dtype,
-              int32_t num_splits, void* workspace, size_t workspace_bytes, int32_t* status,
-              kdt::VerifyParams* pp, WorkspaceLayout* wp) {
+              int32_t num_splits, float split_ratio, void* workspace, size_t workspace_bytes,
+              int32_t* status, kdt::VerifyParams* pp, WorkspaceLayout* wp) {
   if (!q_lat || !q_rope || !kv_lat || !k_rope || !prefix_len || !tree_parent || !q_len ||
       !out_lat || !out_lse)
     return KDTREE_ERR_NULL;
@@ -56,6 +56,7 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
     return KDTREE_ERR_SHAPE;
   if (dtype != KDTREE_DTYPE_FP32 && dtype != KDTREE_DTYPE_BF16) return KDTREE_ERR_DTYPE;
   if (!isfinite(scale)) return KDTREE_ERR_SCALE;
+  if (!(split_ratio > 0.0f && split_ratio <= 1.0f)) return KDTREE_ERR_SPLITS;
   WorkspaceLayout& w = *wp;
   if (!workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &w))
     return KDTREE_ERR_SPLITS;
@@ -80,6 +81,7 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
       num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes + w.part_o_bytes) : nullptr;
   p.status = status;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.split_ratio = split_ratio;
   p.batch = batch;
   p.num_heads = num_heads;
   p.max_q_len = max_q_len;
@@ -131,8 +133,8 @@ size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int
 
 #define KDTREE_SETUP_ARGS                                                                  \
   q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, scale, out_lat, out_lse,  \
-      batch, num_heads, max_q_len, total_q, total_kv, dtype, num_splits, workspace,        \
-      workspace_bytes, status
+      batch, num_heads, max_q_len, total_q, total_kv, dtype, num_splits, split_ratio,      \
+      workspace, workspace_bytes, status
 
 int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv_lat,
                            const void* k_rope, const int32_t* prefix_len,
@@ -140,7 +142,8 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
                            float* out_lat, float* out_lse, void* stream, int32_t batch,
                            int32_t num_heads, int32_t max_q_len, int64_t total_q,
                            int64_t total_kv, int32_t dtype, int32_t num_splits,
-                           void* workspace, size_t workspace_bytes, int32_t* status) {
+                           float split_ratio, void* workspace, size_t workspace_bytes,
+                           int32_t* status) {
   kdt::VerifyParams p;
   WorkspaceLayout w;
   int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
@@ -156,8 +159,8 @@ int32_t kdtree_verify_attn_prepare(const void* q_lat, const void* q_rope, const 
                                    float scale, float* out_lat, float* out_lse, void* stream,
                                    int32_t batch, int32_t num_heads, int32_t max_q_len,
                                    int64_t total_q, int64_t total_kv, int32_t dtype,
-                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                   int32_t* status) {
+                                   int32_t num_splits, float split_ratio, void* workspace,
+                                   size_t workspace_bytes, int32_t* status) {
   kdt::VerifyParams p;
   WorkspaceLayout w;
   int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
@@ -171,8 +174,8 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
                                   float scale, float* out_lat, float* out_lse, void* stream,
                                   int32_t batch, int32_t num_heads, int32_t max_q_len,
                                   int64_t total_q, int64_t total_kv, int32_t dtype,
-                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                  int32_t* status) {
+                                  int32_t num_splits, float split_ratio, void* workspace,
+                                  size_t workspace_bytes, int32_t* status) {
   kdt::VerifyParams p;
   WorkspaceLayout w;
   int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);

@@ -38,6 +38,7 @@ struct VerifyParams {
   void* k16;         // bf16 path: fp16 latent tiles (32 keys each) written by the pre-pass
   int32_t* order;    // bf16 path: requests by descending KV length (written by the pre-pass)
   float scale_log2;  // scale * log2(e)
+  float split_ratio; // 1: equal splits; < 1: geometric splits, largest first
   int32_t batch, num_heads, max_q_len, num_splits, m_tiles;
   int64_t total_q, total_kv;
   int64_t k16_tiles; // capacity of `k16` in tiles
@@ -94,6 +95,26 @@ struct SampleParams {
   uint64_t seed, offset;
   int32_t* tokens;      // [rows]
 };
+
+// First key of split s (0..S) of a request with P prefix keys.  Splits cover whole
+// 32-key tiles (every split after the first starts on a tile boundary), and the tree tail
+// goes with split S-1.  ratio 1: S equal chunks of ceil(P/S) keys rounded up to 32.
+// ratio r < 1: split s holds about r^s (1 - r) / (1 - r^S) of the prefix, largest first,
+// so that when the launch's last round is short it holds the smallest pieces.  Both ends of
+// a split come from this one function, so neighbouring splits meet exactly.
+__device__ __forceinline__ int split_begin(int P, int S, float r, int s) {
+  if (s <= 0) return 0;
+  if (s >= S) return P;
+  int64_t b;
+  if (!(r < 1.0f)) {
+    const int64_t chunk = (((int64_t)P + S - 1) / S + 31) / 32 * 32;
+    b = (int64_t)s * chunk;
+  } else {
+    const float f = (1.0f - __builtin_powf(r, (float)s)) / (1.0f - __builtin_powf(r, (float)S));
+    b = ((int64_t)((float)P * f) + 31) / 32 * 32;
+  }
+  return (int)(b < P ? b : P);
+}
 
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_sample_tokens(const SampleParams& p, bool bf16, hipStream_t stream);

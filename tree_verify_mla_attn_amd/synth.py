@@ -165,6 +165,7 @@ class VerifyInputs:
     num_heads: int
     num_splits: int = 1
     name: str = ""
+    split_ratio: float = 1.0
 
     @property
     def batch(self) -> int:
@@ -244,18 +245,20 @@ def make_inputs(rng: np.random.Generator, *, num_heads: int, prefix_lens: Sequen
 # The five workloads: batch, heads, prefix, draft budget / top-K, dtype, and the split-KV
 # launch configuration (workload 5 prescribes 16 chunks; the others use the count that
 # ran fastest on MI355X: small fp32 batches need splits to occupy the chip, and the best
-# counts keep the workgroups (row tiles x splits) within one round of the 256 CUs).
+# counts keep the workgroups (row tiles x splits) within one round of the 256 CUs).  Where
+# the workgroups overrun whole rounds of the CUs (workload 3: 528 on 256; workload 5:
+# 2112), geometric chunk sizes (split_ratio < 1, largest first) ran fastest in sweeps.
 CONFIGS = {
     1: dict(name="tiny_b1_p256_q9_fp32", batch=1, heads=64, prefix=256, top_k=[8], budget=8,
             dtype="fp32", num_splits=12),
     2: dict(name="b1_p2048_q33_wide_fp32", batch=1, heads=64, prefix=2048, top_k=[8], budget=32,
             dtype="fp32", num_splits=7),
     3: dict(name="b8_p4096_q65_deep_bf16", batch=8, heads=64, prefix=4096, top_k=[2], budget=64,
-            dtype="bf16", num_splits=2),
+            dtype="bf16", num_splits=2, split_ratio=0.4),
     4: dict(name="b64_ragged1024-8192_q33_mixed_bf16", batch=64, heads=64, prefix=(1024, 8192),
             top_k=[8] * 32 + [2] * 32, budget=32, dtype="bf16", num_splits=1),
     5: dict(name="b4_p32768_q65_split16_bf16", batch=4, heads=64, prefix=32768, top_k=[4],
-            budget=64, dtype="bf16", num_splits=16),
+            budget=64, dtype="bf16", num_splits=16, split_ratio=0.85),
 }
 
 
@@ -279,16 +282,19 @@ def config_trees(cfg: int, rng: Optional[np.random.Generator] = None):
     return rng, prefix, parents
 
 
-def config_inputs(cfg: int, num_splits: Optional[int] = None) -> VerifyInputs:
+def config_inputs(cfg: int, num_splits: Optional[int] = None,
+                  split_ratio: Optional[float] = None) -> VerifyInputs:
     """Seeded inputs of workload ``cfg`` (1..5): rng = default_rng(1000 + cfg).
 
     Draw order: prefix lengths (ragged workload only), per-request log-prob tables
     and trees, then q_lat, q_rope, kv_lat, k_rope."""
     c = CONFIGS[cfg]
     rng, prefix, parents = config_trees(cfg)
-    return make_inputs(rng, num_heads=c["heads"], prefix_lens=prefix, parents=parents,
-                       dtype=c["dtype"], num_splits=num_splits or c["num_splits"],
-                       name=c["name"])
+    inp = make_inputs(rng, num_heads=c["heads"], prefix_lens=prefix, parents=parents,
+                      dtype=c["dtype"], num_splits=num_splits or c["num_splits"],
+                      name=c["name"])
+    inp.split_ratio = split_ratio if split_ratio is not None else c.get("split_ratio", 1.0)
+    return inp
 
 
 def device_tensors(inp: VerifyInputs, device="cuda"):
