@@ -406,7 +406,8 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     # Events on the launch stream: ev[i] -> mid[i] is the pre-pass (bf16 inputs),
-    # mid[i] -> ev[i + 1] the attention kernel (+ the merge when num_splits > 1).
+    # mid[i] -> ev[i + 1] the attention kernel (+ the partial-lse fill and the merge when
+    # num_splits > 1).
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
