@@ -37,6 +37,7 @@ typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -53,6 +54,12 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 constexpr int K16_ROW = 68;
 constexpr int K16_U4 = BN * K16_ROW, KROPE_U4 = BN * 8;
 constexpr int K16_STEP16 = 16 * K16_ROW * 16;  // bytes between key rows r and r + 16
+// Output staging in the finished tile ring: 32 rows x 128 fp32 features per wave, rows
+// padded by 16 bytes so that both the row-per-lane writes and the row-contiguous reads are
+// free of bank conflicts; two waves' blocks fit in one latent tile buffer.
+constexpr int EPI_ROW_BYTES = 128 * 4 + 16;
+constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW_BYTES;
+static_assert(2 * EPI_WAVE_BYTES <= K16_U4 * 16, "two output blocks per tile buffer");
 // Separate objects per stage: the compiler's wait-count insertion can then tell that a
 // DMA into one stage does not alias LDS reads of another, and does not stall the
 // compute of tile j on the in-flight copy of tile j+2.
@@ -305,6 +312,14 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const f16x8 (&pk)[2], i
 // Wait states between the last PV MFMA and VALU reads of the accumulators.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n s_nop 7\n s_nop 3"); }
 
+// Orders one wave's LDS writes before its later LDS reads (and the reverse): the wave's
+// LDS instructions execute in order, so only the compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // max / sum of x over the lane pair (l, l ^ 32) that shares a query row, without an
 // LDS round trip: v_permlane32_swap exchanges the upper half of one copy with the lower
 // half of the other, so every lane ends up with both values of its pair.
@@ -323,6 +338,15 @@ __device__ __forceinline__ float pair_sum(float x) {
 // VGPR home.
 __device__ __forceinline__ f32x16 read_acc(const f32x16& acc) {
   f32x16 t = acc;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+// The same copy, pinned after everything before it in program order: the first empty asm
+// keeps the value in AGPRs up to this point, so the register allocator cannot hoist the
+// copy (and its 16 VGPRs) above earlier barriers.
+__device__ __forceinline__ f32x16 read_acc_here(const f32x16& acc) {
+  f32x16 t = acc;
+  asm volatile("" : "+a"(t));
   asm volatile("" : "+v"(t));
   return t;
 }
@@ -653,28 +677,60 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const float l_tot = pair_sum(st.l);
   const float inv = 1.0f / l_tot;
   const float lse = st.m * LN2 + logf(l_tot);
-  if (!row_ok) return;
-  float* out;
-  float* lse_out;
-  if (S == 1) {
-    out = p.out_lat + grow * DL;
-    lse_out = p.out_lse + grow;
-  } else {
-    out = p.part_o + ((int64_t)split * p.total_q * H + grow) * DL;
-    lse_out = p.part_lse + (int64_t)split * p.total_q * H + grow;
-  }
+  // A wave's 32 rows are consecutive global rows, so its output block is contiguous.
+  const int wrow0 = m0 + wave * 32;
+  const int wrows = min(32, rows - wrow0);  // rows of this wave that exist (may be <= 0)
+  const int64_t gbase = qoff * H + wrow0;
+  float* const out = S == 1 ? p.out_lat + gbase * DL
+                             : p.part_o + ((int64_t)split * p.total_q * H + gbase) * DL;
+  // The accumulator layout gives each lane 16-byte pieces of one row, so direct stores
+  // would touch 32 rows per instruction.  Instead each wave passes its block through LDS
+  // (the tile ring, free once every wave has finished the last tile), 128 features at a
+  // time, and every store instruction then writes 512 contiguous bytes of two rows.
+  // No wave has a tile read or copy outstanding here (the last trip waited for its reads
+  // before its MFMAs, and issued no copy), so a bare barrier suffices.
+  asm volatile("s_barrier" ::: "memory");
+  if (wrows <= 0) return;
+  LDS_AS char* stage = (LDS_AS char*)(LDS_AS void*)((wave < 2) ? sK16a : sK16b) + (wave & 1) * EPI_WAVE_BYTES;
+  const int r = lane & 31;
 #pragma unroll
-  for (int fb = 0; fb < 16; ++fb) {
-    const f32x16 t = read_acc(o[fb]);
+  for (int chunk = 0; chunk < 4; ++chunk) {
+    // keep each chunk's accumulator reads inside the chunk: read all at once, the 256
+    // values would not fit the VGPRs next to the accumulators
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float4 v = make_float4(t[4 * q4] * inv, t[4 * q4 + 1] * inv, t[4 * q4 + 2] * inv,
-                             t[4 * q4 + 3] * inv);
-      *(float4*)(out + fb * 32 + q4 * 8 + h * 4) = v;
+    for (int f4 = 0; f4 < 4; ++f4) {
+      const f32x16 t = read_acc_here(o[chunk * 4 + f4]);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = {t[4 * q4] * inv, t[4 * q4 + 1] * inv, t[4 * q4 + 2] * inv,
+                         t[4 * q4 + 3] * inv};
+        *(LDS_AS f32x4*)(stage + r * EPI_ROW_BYTES + (f4 * 32 + q4 * 8 + h * 4) * 4) = v;
+      }
     }
+    wave_sync();
+    f32x4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = *(const LDS_AS f32x4*)(stage + (2 * i + h) * EPI_ROW_BYTES + r * 16);
+    float* dst = out + (int64_t)h * DL + chunk * 128 + r * 4;
+    if (wrows == 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (2 * i + h < wrows) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
+    }
+    wave_sync();
   }
-  if (h == 0) {
-    *lse_out = lse;
+  // last, so that no global store is outstanding when the first LDS write above waits
+  // for the tile copies
+  if (row_ok && h == 0) {
+    if (S == 1)
+      p.out_lse[grow] = lse;
+    else
+      p.part_lse[(int64_t)split * p.total_q * H + grow] = lse;
     if (!(fabsf(lse) < INFINITY) && p.status) atomicOr(p.status, ST_NONFINITE);
   }
 }
