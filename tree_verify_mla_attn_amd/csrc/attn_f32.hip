@@ -32,6 +32,11 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int LSTRIDE = DL + 4;
 constexpr int STAGE_LAT = BN * LSTRIDE;
 constexpr int STAGE_FLOATS = STAGE_LAT + BN * DR;
+// Output staging in the finished tile stages: 16 rows x 256 fp32 features per wave, rows
+// padded by 16 bytes (conflict-free row-per-lane writes); two waves' blocks per stage.
+constexpr int EPI_ROW_BYTES = 256 * 4 + 16;
+constexpr int EPI_WAVE_BYTES = 16 * EPI_ROW_BYTES;
+static_assert(2 * EPI_WAVE_BYTES <= STAGE_FLOATS * 4, "two output blocks per stage");
 // Separate objects per stage: the compiler's wait-count insertion can then tell that a
 // copy into one stage does not alias reads of the other.
 __shared__ __attribute__((aligned(1024))) float sK0[STAGE_FLOATS];
@@ -316,22 +321,49 @@ void verify_attn_f32_kernel(VerifyParams p) {
   l_tot += __shfl_xor(l_tot, 32);
   const float inv = 1.0f / l_tot;
   const float lse = st.m * LN2 + logf(l_tot);
-  if (!row_ok) return;
-  float* out;
-  float* lse_out;
-  if (S == 1) {
-    out = p.out_lat + grow * DL;
-    lse_out = p.out_lse + grow;
-  } else {
-    out = p.part_o + ((int64_t)split * p.total_q * H + grow) * DL;
-    lse_out = p.part_lse + (int64_t)split * p.total_q * H + grow;
-  }
+  // A wave's 16 rows are consecutive global rows, so its output block is contiguous.
+  const int wrow0 = m0 + wave * 16;
+  const int wrows = min(16, rows - wrow0);  // rows of this wave that exist (may be <= 0)
+  const int64_t gbase = qoff * H + wrow0;
+  float* const out = S == 1 ? p.out_lat + gbase * DL
+                            : p.part_o + ((int64_t)split * p.total_q * H + gbase) * DL;
+  // Each lane holds 16-byte pieces of one row, so direct stores would touch 16 rows per
+  // instruction.  Each wave passes its block through LDS (the tile stages, free once every
+  // wave has finished the last tile), 256 features at a time; every store instruction then
+  // writes 1 KB of one row.  No tile copy is in flight here (the last trips issue none).
+  __syncthreads();
+  if (wrows > 0) {
+    LDS_AS char* stage =
+        (LDS_AS char*)(LDS_AS void*)((wave < 2) ? sK0 : sK1) + (wave & 1) * EPI_WAVE_BYTES;
+    const int r = lane & 15;
 #pragma unroll
-  for (int fb = 0; fb < 32; ++fb)
-    *(float4*)(out + fb * 16 + g * 4) =
-        make_float4(o[fb][0] * inv, o[fb][1] * inv, o[fb][2] * inv, o[fb][3] * inv);
-  if (g == 0) {
-    *lse_out = lse;
+    for (int chunk = 0; chunk < 2; ++chunk) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) {
+        const f32x4 a = o[chunk * 16 + f];
+        *(LDS_AS f32x4*)(stage + r * EPI_ROW_BYTES + (f * 16 + g * 4) * 4) =
+            f32x4{a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      f32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = *(const LDS_AS f32x4*)(stage + i * EPI_ROW_BYTES + lane * 16);
+      float* dst = out + chunk * 256 + lane * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < wrows) *(f32x4*)(dst + (int64_t)i * DL) = v[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  if (row_ok && g == 0) {
+    if (S == 1)
+      p.out_lse[grow] = lse;
+    else
+      p.part_lse[(int64_t)split * p.total_q * H + grow] = lse;
     if (!(fabsf(lse) < INFINITY) && p.status) atomicOr(p.status, ST_NONFINITE);
   }
 }
