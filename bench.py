@@ -143,8 +143,9 @@ def cpu_baseline(inp, seconds):
 def sharded_share(B, synth, torch, dev, parts=8, steps=20):
     """One GPU's share of the 32768-key workload under context parallelism across `parts`
     GPUs: the same 4 requests and trees, 32768 / parts prefix keys each, giving that GPU's
-    partial output and log-sum-exp (num_splits chosen as for a single GPU); the
-    cross-GPU merge would be the same LSE merge the split path runs."""
+    partial output and log-sum-exp (num_splits and split_ratio chosen by the host-side
+    helpers, as for a single GPU); the cross-GPU merge would be the same LSE merge the
+    split path runs."""
     import numpy as np
     c = synth.CONFIGS[5]
     rng, prefix, parents = synth.config_trees(5)
@@ -152,8 +153,9 @@ def sharded_share(B, synth, torch, dev, parts=8, steps=20):
     inp = synth.make_inputs(rng, num_heads=c["heads"], prefix_lens=share, parents=parents,
                             dtype=c["dtype"])
     d = synth.device_tensors(inp, dev)
-    splits = B.choose_num_splits(inp.batch, inp.num_heads, inp.max_q_len,
-                                 float(np.mean(share)) + inp.max_q_len)
+    mean_kv = float(np.mean(share)) + inp.max_q_len
+    splits = B.choose_num_splits(inp.batch, inp.num_heads, inp.max_q_len, mean_kv)
+    ratio = B.choose_split_ratio(inp.batch, inp.num_heads, inp.max_q_len, mean_kv, splits)
     call = B.VerifyAttn()
     out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)
@@ -164,7 +166,7 @@ def sharded_share(B, synth, torch, dev, parts=8, steps=20):
     def run():
         call(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
              d["tree_parent"], d["q_len"], inp.scale, out_lat=out, out_lse=lse,
-             num_splits=splits, max_q_len=inp.max_q_len, workspace=ws)
+             num_splits=splits, max_q_len=inp.max_q_len, workspace=ws, split_ratio=ratio)
     for _ in range(3):
         run()
     torch.cuda.synchronize(dev)
@@ -176,7 +178,7 @@ def sharded_share(B, synth, torch, dev, parts=8, steps=20):
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
     return {"workload": f"{c['name']} / {parts}-way context share", "prefix_per_gpu": share[0],
-            "num_splits": splits, "ms": round(ms, 5),
+            "num_splits": splits, "split_ratio": ratio, "ms": round(ms, 5),
             "TFLOPs": round(inp.algorithmic_flops() / (ms * 1e-3) / 1e12, 2),
             "merge_message_MB_per_gpu": round(inp.total_q * inp.num_heads * 513 * 4 / 1e6, 1)}
 

@@ -125,6 +125,29 @@ def test_choose_num_splits():
     assert B.choose_num_splits(4, 64, 65, 32833) > 1
 
 
+def test_choose_split_ratio():
+    # the ratios sweeps on MI355X found fastest (bf16): 0.35-0.4 for 8 requests of
+    # 4096 + 65 keys at 2 splits, 0.85 (0.82-0.88 within noise) for 4 of 32768 + 65 at 16
+    assert 0.35 <= B.choose_split_ratio(8, 64, 65, 4161, 2) <= 0.45
+    assert 0.8 <= B.choose_split_ratio(4, 64, 65, 32833, 16) <= 0.9
+    # nothing to balance: one split, or workgroups that fill whole rounds of every XCD
+    assert B.choose_split_ratio(64, 64, 33, 4790, 1) == 1.0
+    assert B.choose_split_ratio(8, 64, 64, 4096, 4) == 1.0
+    # the fp32 launch of the 2048-key prefix fits one round at 7 splits
+    assert B.choose_split_ratio(1, 64, 33, 2081, 7, dtype=B.KDTREE_DTYPE_FP32) == 1.0
+    # a geometric ratio that would leave a split empty is never chosen (equal splits of
+    # a short prefix may be, as the kernels allow)
+    chosen = []
+    for batch, mean_kv in ((8, 4161), (3, 2000), (2, 300)):
+        for s in (2, 3, 4, 6, 8, 12, 16, 64):
+            r = B.choose_split_ratio(batch, 64, 65, mean_kv, s)
+            if r < 1.0:
+                chosen.append(r)
+                ends = [B._split_begin(mean_kv - 65, s, r, k) for k in range(s + 1)]
+                assert all(b < e for b, e in zip(ends[:-2], ends[1:-1])), (s, r, ends)
+    assert len(chosen) >= 5
+
+
 # ---------------------------------------------------------------- builder and accept
 def _build(**kw):
     args = dict(logp=FAKE, token_ids=FAKE, root_token=FAKE, batch=2, depth=15, top_k=8,

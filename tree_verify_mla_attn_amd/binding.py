@@ -12,6 +12,7 @@ There is no fallback: if the library is missing or fails to load, every call rai
 from __future__ import annotations
 
 import ctypes
+import heapq
 import math
 import os
 from typing import Optional
@@ -285,6 +286,72 @@ def choose_num_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float
         if chunk <= 32:
             break
     return best
+
+
+def _split_begin(prefix: int, num_splits: int, ratio: float, s: int) -> int:
+    # host copy of the kernels' split boundaries (whole 32-key tiles, largest split first
+    # for ratio < 1), used only by the schedule model below
+    if s <= 0:
+        return 0
+    if s >= num_splits:
+        return prefix
+    if ratio >= 1.0:
+        b = s * (((prefix + num_splits - 1) // num_splits + 31) // 32 * 32)
+    else:
+        f = (1.0 - ratio ** s) / (1.0 - ratio ** num_splits)
+        b = (int(prefix * f) + 31) // 32 * 32
+    return min(b, prefix)
+
+
+def choose_split_ratio(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
+                       num_splits: int, dtype: int = KDTREE_DTYPE_BF16, n_xcd: int = 8,
+                       cu_per_xcd: int = 32, overhead_keys: int = 500) -> float:
+    """Host-side choice of split_ratio for a given split count, from a schedule model.
+
+    Each workgroup costs its split's keys (whole 32-key tiles) plus ~overhead_keys.  The
+    model deals workgroups to XCDs as the kernels do (bf16: groups of row tiles of one
+    request and split, snake order over the XCDs, request-major for equal splits and
+    split-major for geometric ones; fp32: workgroup i to XCD i mod 8), list-schedules
+    each XCD's queue on its CUs, and returns the ratio in {1, 0.95, ..., 0.05} with the
+    shortest makespan (1 unless another is more than 1% shorter), among the ratios that
+    leave no split empty.  Requests are taken as equal, mean_kv keys each.  On MI355X it reproduces the swept optima: 0.4 for 8
+    requests of 4096 + 65 keys at 2 splits, 0.85 for 4 of 32768 + 65 at 16 splits."""
+    if num_splits <= 1:
+        return 1.0
+    rows_per_block = 128 if dtype == KDTREE_DTYPE_BF16 else 64
+    m_tiles = math.ceil(max_q_len * num_heads / rows_per_block)
+    prefix = max(0, int(round(mean_kv)) - max_q_len)
+
+    def makespan(ratio: float) -> float:
+        geo = ratio < 1.0
+        cost = []
+        for split in range(num_splits):
+            kb = _split_begin(prefix, num_splits, ratio, split) & ~31
+            ke = (prefix + max_q_len if split == num_splits - 1
+                  else _split_begin(prefix, num_splits, ratio, split + 1))
+            if ke <= kb:  # an empty split: fewer splits would do the same work
+                return math.inf
+            cost.append(math.ceil((ke - kb) / 32) * 32 + overhead_keys)
+        queues = [[] for _ in range(n_xcd)]
+        for g in range(batch * num_splits):
+            split = g // batch if geo else g % num_splits
+            if dtype == KDTREE_DTYPE_BF16:
+                rnd, x = divmod(g, n_xcd)
+                queues[(n_xcd - 1 - x) if rnd & 1 else x] += [cost[split]] * m_tiles
+            else:
+                for t in range(m_tiles):
+                    queues[(g * m_tiles + t) % n_xcd].append(cost[split])
+        worst = 0.0
+        for q in queues:
+            cus = [0.0] * cu_per_xcd
+            for c in q:
+                heapq.heappush(cus, heapq.heappop(cus) + c)
+            worst = max(worst, max(cus))
+        return worst
+
+    equal = makespan(1.0)
+    best, best_r = min((makespan(k / 20), -k / 20) for k in range(1, 20))
+    return -best_r if best < 0.99 * equal else 1.0
 
 
 class VerifyAttn:
