@@ -144,8 +144,8 @@ def sharded_share(B, synth, torch, dev, parts=8, steps=20):
     """One GPU's share of the 32768-key workload under context parallelism across `parts`
     GPUs: the same 4 requests and trees, 32768 / parts prefix keys each, giving that GPU's
     partial output and log-sum-exp (num_splits and split_ratio chosen by the host-side
-    helpers, as for a single GPU); the cross-GPU merge would be the same LSE merge the
-    split path runs."""
+    schedule model, as for a single GPU); the cross-GPU merge would be the same LSE merge
+    the split path runs."""
     import numpy as np
     c = synth.CONFIGS[5]
     rng, prefix, parents = synth.config_trees(5)
@@ -154,8 +154,7 @@ def sharded_share(B, synth, torch, dev, parts=8, steps=20):
                             dtype=c["dtype"])
     d = synth.device_tensors(inp, dev)
     mean_kv = float(np.mean(share)) + inp.max_q_len
-    splits = B.choose_num_splits(inp.batch, inp.num_heads, inp.max_q_len, mean_kv)
-    ratio = B.choose_split_ratio(inp.batch, inp.num_heads, inp.max_q_len, mean_kv, splits)
+    splits, ratio = B.choose_splits(inp.batch, inp.num_heads, inp.max_q_len, mean_kv)
     call = B.VerifyAttn()
     out = torch.empty((inp.total_q, inp.num_heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((inp.total_q, inp.num_heads), dtype=torch.float32, device=dev)

@@ -148,6 +148,14 @@ def test_choose_split_ratio():
     assert len(chosen) >= 5
 
 
+def test_choose_splits():
+    # (count, ratio) pairs that ran fastest of those timed on MI355X (bf16, 64 heads)
+    assert B.choose_splits(4, 64, 65, 4161) == (4, 0.75)    # 2..8 splits timed
+    assert B.choose_splits(8, 64, 65, 4161) == (2, 0.4)     # 2..4 splits timed
+    assert B.choose_splits(4, 64, 65, 32833) == (8, 0.75)   # 8, 12, 16 timed
+    assert B.choose_splits(64, 64, 33, 5120) == (1, 1.0)    # the batch-64 launch
+
+
 # ---------------------------------------------------------------- builder and accept
 def _build(**kw):
     args = dict(logp=FAKE, token_ids=FAKE, root_token=FAKE, batch=2, depth=15, top_k=8,

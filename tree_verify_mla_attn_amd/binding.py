@@ -288,6 +288,9 @@ def choose_num_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float
     return best
 
 
+DL_BYTES = 512 * 4  # one fp32 latent output row
+
+
 def _split_begin(prefix: int, num_splits: int, ratio: float, s: int) -> int:
     # host copy of the kernels' split boundaries (whole 32-key tiles, largest split first
     # for ratio < 1), used only by the schedule model below
@@ -303,9 +306,43 @@ def _split_begin(prefix: int, num_splits: int, ratio: float, s: int) -> int:
     return min(b, prefix)
 
 
+def _schedule_makespan(batch: int, m_tiles: int, prefix: int, q: int, num_splits: int,
+                       ratio: float, bf16: bool, n_xcd: int, cu_per_xcd: int,
+                       overhead_keys: int) -> float:
+    # Makespan (in key units) of one launch of equal requests: each workgroup costs its
+    # split's keys (whole 32-key tiles) plus overhead_keys; workgroups are dealt to XCDs
+    # as the kernels deal them and list-scheduled on each XCD's CUs.  inf when a split
+    # would be empty (fewer splits would do the same work).
+    cost = []
+    for split in range(num_splits):
+        kb = _split_begin(prefix, num_splits, ratio, split) & ~31
+        ke = (prefix + q if split == num_splits - 1
+              else _split_begin(prefix, num_splits, ratio, split + 1))
+        if ke <= kb:
+            return math.inf
+        cost.append(math.ceil((ke - kb) / 32) * 32 + overhead_keys)
+    geo = ratio < 1.0
+    queues = [[] for _ in range(n_xcd)]
+    for g in range(batch * num_splits):
+        split = g // batch if geo else g % num_splits
+        if bf16:  # groups of m_tiles row tiles, snake order over the XCDs
+            rnd, x = divmod(g, n_xcd)
+            queues[(n_xcd - 1 - x) if rnd & 1 else x] += [cost[split]] * m_tiles
+        else:     # workgroup i on XCD i mod n_xcd
+            for t in range(m_tiles):
+                queues[(g * m_tiles + t) % n_xcd].append(cost[split])
+    worst = 0.0
+    for queue in queues:
+        cus = [0.0] * cu_per_xcd
+        for c in queue:
+            heapq.heappush(cus, heapq.heappop(cus) + c)
+        worst = max(worst, max(cus))
+    return worst
+
+
 def choose_split_ratio(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
                        num_splits: int, dtype: int = KDTREE_DTYPE_BF16, n_xcd: int = 8,
-                       cu_per_xcd: int = 32, overhead_keys: int = 500) -> float:
+                       cu_per_xcd: int = 32, overhead_keys: int = 600) -> float:
     """Host-side choice of split_ratio for a given split count, from a schedule model.
 
     Each workgroup costs its split's keys (whole 32-key tiles) plus ~overhead_keys.  The
@@ -314,45 +351,60 @@ def choose_split_ratio(batch: int, num_heads: int, max_q_len: int, mean_kv: floa
     split-major for geometric ones; fp32: workgroup i to XCD i mod 8), list-schedules
     each XCD's queue on its CUs, and returns the ratio in {1, 0.95, ..., 0.05} with the
     shortest makespan (1 unless another is more than 1% shorter), among the ratios that
-    leave no split empty.  Requests are taken as equal, mean_kv keys each.  On MI355X it reproduces the swept optima: 0.4 for 8
-    requests of 4096 + 65 keys at 2 splits, 0.85 for 4 of 32768 + 65 at 16 splits."""
+    leave no split empty.  Requests are taken as equal, mean_kv keys each.  On MI355X it
+    reproduces the swept optima: 0.4 for 8 requests of 4096 + 65 keys at 2 splits, 0.85
+    for 4 of 32768 + 65 at 16 splits."""
     if num_splits <= 1:
         return 1.0
-    rows_per_block = 128 if dtype == KDTREE_DTYPE_BF16 else 64
-    m_tiles = math.ceil(max_q_len * num_heads / rows_per_block)
+    bf16 = dtype == KDTREE_DTYPE_BF16
+    m_tiles = math.ceil(max_q_len * num_heads / (128 if bf16 else 64))
     prefix = max(0, int(round(mean_kv)) - max_q_len)
-
-    def makespan(ratio: float) -> float:
-        geo = ratio < 1.0
-        cost = []
-        for split in range(num_splits):
-            kb = _split_begin(prefix, num_splits, ratio, split) & ~31
-            ke = (prefix + max_q_len if split == num_splits - 1
-                  else _split_begin(prefix, num_splits, ratio, split + 1))
-            if ke <= kb:  # an empty split: fewer splits would do the same work
-                return math.inf
-            cost.append(math.ceil((ke - kb) / 32) * 32 + overhead_keys)
-        queues = [[] for _ in range(n_xcd)]
-        for g in range(batch * num_splits):
-            split = g // batch if geo else g % num_splits
-            if dtype == KDTREE_DTYPE_BF16:
-                rnd, x = divmod(g, n_xcd)
-                queues[(n_xcd - 1 - x) if rnd & 1 else x] += [cost[split]] * m_tiles
-            else:
-                for t in range(m_tiles):
-                    queues[(g * m_tiles + t) % n_xcd].append(cost[split])
-        worst = 0.0
-        for q in queues:
-            cus = [0.0] * cu_per_xcd
-            for c in q:
-                heapq.heappush(cus, heapq.heappop(cus) + c)
-            worst = max(worst, max(cus))
-        return worst
-
-    equal = makespan(1.0)
-    best, best_r = min((makespan(k / 20), -k / 20) for k in range(1, 20))
+    span = lambda r: _schedule_makespan(batch, m_tiles, prefix, max_q_len, num_splits, r,
+                                        bf16, n_xcd, cu_per_xcd, overhead_keys)
+    equal = span(1.0)
+    best, best_r = min((span(k / 20), -k / 20) for k in range(1, 20))
     return -best_r if best < 0.99 * equal else 1.0
 
+
+def choose_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
+                  n_xcd: int = 8, cu_per_xcd: int = 32, overhead_keys: int = 600,
+                  us_per_key: float = 1.79 / 32, merge_gbs: float = 4300.0,
+                  merge_fixed_us: float = 6.0) -> tuple:
+    """(num_splits, split_ratio) for bf16 inputs: for each split count, the ratio of
+    choose_split_ratio(), priced as the schedule model's makespan (us_per_key: one
+    32-key tile per ~1.79 us on MI355X) plus the split path's fill and merge (its
+    partials read once, the output written once, at ~merge_gbs GB/s).  Returns the
+    cheapest pair, fewer splits on ties.  Its picks matched the fastest of those timed on
+    MI355X for 4 requests with 65-node trees and 64 heads: 4 splits at ratio 0.75 for
+    4096-key prefixes (0.251 ms; 3 equal splits 0.301 ms), 8 at 0.75 for 32768-key ones
+    (1.148 ms; 16 at 0.85 1.247 ms); 2 at 0.4 for 8 requests of 4096 keys."""
+    m_tiles = math.ceil(max_q_len * num_heads / 128)
+    prefix = max(0, int(round(mean_kv)) - max_q_len)
+    rows = batch * max_q_len * num_heads
+    best = None
+    for s in range(1, 65):
+        # a bound that only grows with s: the work spread evenly over every CU, plus the
+        # merge; once it reaches the best time so far, no larger count can beat it
+        bound = (batch * m_tiles * (prefix + max_q_len + s * overhead_keys) * us_per_key
+                 / (n_xcd * cu_per_xcd))
+        if s > 1:
+            bound += (s + 1) * rows * (DL_BYTES + 4) / (merge_gbs * 1e3) + merge_fixed_us
+        if best is not None and bound >= best[0]:
+            break
+        r = choose_split_ratio(batch, num_heads, max_q_len, mean_kv, s, KDTREE_DTYPE_BF16,
+                               n_xcd, cu_per_xcd, overhead_keys)
+        span = _schedule_makespan(batch, m_tiles, prefix, max_q_len, s, r, True, n_xcd,
+                                  cu_per_xcd, overhead_keys)
+        if span == math.inf:
+            continue
+        t = span * us_per_key
+        if s > 1:
+            t += (s + 1) * rows * (DL_BYTES + 4) / (merge_gbs * 1e3) + merge_fixed_us
+        if best is None or t < best[0]:
+            best = (t, s, r)
+        if (prefix + s - 1) // s <= 32:
+            break
+    return best[1], best[2]
 
 class VerifyAttn:
     """Reusable call object: checks and caches shapes, allocates outputs / workspace with
