@@ -79,7 +79,9 @@ extern "C" {
 #define KDTREE_STATUS_BAD_PARENT 4u   /* parent[0] != -1 or parent[i] outside [0, i) */
 #define KDTREE_STATUS_OVERFLOW 8u     /* packed offsets exceed total_q / total_kv, or a
                                          request has prefix_len + q_len > 2^24 */
-#define KDTREE_STATUS_NONFINITE 16u   /* a non-finite output row was produced */
+#define KDTREE_STATUS_NONFINITE 16u   /* a non-finite output row was produced (with the
+                                         bf16 last-round cut, such a row of a cut row
+                                         tile may be left unwritten instead) */
 
 /* MAX_QLEN (65). */
 int32_t kdtree_max_qlen(void);
@@ -89,8 +91,16 @@ int32_t kdtree_max_qlen(void);
  *   bf16 inputs: the request schedule (batch int32) and fp16 copies of the latent rows,
  *     key-major in 32-key tiles, both written by a pre-pass of the same call:
  *     batch * 4 and (total_kv / 32 + batch + 1) * 32 KB bytes;
- *   num_splits > 1: split partial outputs num_splits * total_q * num_heads * 512 * 4
- *     bytes and their log-sum-exps num_splits * total_q * num_heads * 4 bytes. */
+ *   one region of the larger of
+ *     num_splits > 1: split partial outputs num_splits * total_q * num_heads * 512 * 4
+ *       bytes, then their log-sum-exps num_splits * total_q * num_heads * 4 bytes;
+ *     bf16 inputs: 256 * 128 * (512 + 1) * 4 + 256 * 16 bytes, used with num_splits
+ *       == 1 by the last-round cut (when each of the 8 XCDs' queues holds at most two
+ *       whole rounds of 32 workgroups, the row tiles left over after them run as key
+ *       pieces over all of the XCD's CUs, and a merge pass combines the pieces; same
+ *       result up to rounding).
+ * The size never decreases with num_splits, so a workspace sized for some split count
+ * also serves every smaller one. */
 size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int32_t batch,
                                           int32_t num_heads, int32_t num_splits, int32_t dtype);
 

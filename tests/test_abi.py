@@ -49,13 +49,22 @@ def test_workspace_bytes():
         return -(-x // 256) * 256
     # fp32, one split: nothing
     assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 0) == 0
-    # bf16, one split: the request order and the fp16 latent tiles only
-    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 1) == up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768)
-    # bf16, 16 splits: tiles + partial outputs + partial lse
+    # bf16, one split: the request order, the fp16 latent tiles, and the area of the
+    # last-round cut (256 pieces x 128 rows x (512 + 1) fp32, then 256 x 2 int64)
+    pieces = 256 * 128 * 513 * 4 + 256 * 16
+    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 1) == up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768) + pieces
+    # bf16, 16 splits: tiles + partial outputs + partial lse (larger than the cut area,
+    # which shares their region)
     tq, tkv, b, h, s = 260, 131332, 4, 64, 16
     rows = tq * h
     want = up(b * 4) + up((tkv // 32 + b + 1) * 32768) + up(s * rows * 512 * 4) + up(s * rows * 4)
     assert B.kdtree_verify_attn_workspace_bytes(tq, tkv, b, h, s, 1) == want
+    # bf16, 2 splits of a small batch: the cut area is the larger
+    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 2, 1) == up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768) + pieces
+    # never smaller for more splits
+    for dt in (0, 1):
+        sizes = [B.kdtree_verify_attn_workspace_bytes(165, 1500, 5, 64, k, dt) for k in range(1, 40)]
+        assert sizes == sorted(sizes)
     # fp32, splits: partials only
     assert B.kdtree_verify_attn_workspace_bytes(tq, tkv, b, h, s, 0) == up(s * rows * 512 * 4) + up(s * rows * 4)
     for bad in [(0, 10, 1, 64, 2, 1), (10, 10, 1, 64, 0, 1), (10, 10, 1, 64, 257, 1),
@@ -151,7 +160,7 @@ def test_choose_split_ratio():
 def test_choose_splits():
     # (count, ratio) pairs that ran fastest of those timed on MI355X (bf16, 64 heads)
     assert B.choose_splits(4, 64, 65, 4161) == (4, 0.75)    # 2..8 splits timed
-    assert B.choose_splits(8, 64, 65, 4161) == (2, 0.4)     # 2..4 splits timed
+    assert B.choose_splits(8, 64, 65, 4161) == (1, 1.0)     # with the last-round cut
     assert B.choose_splits(4, 64, 65, 32833) == (8, 0.75)   # 8, 12, 16 timed
     assert B.choose_splits(64, 64, 33, 5120) == (1, 1.0)    # the batch-64 launch
 

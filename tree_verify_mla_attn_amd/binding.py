@@ -331,6 +331,15 @@ def _schedule_makespan(batch: int, m_tiles: int, prefix: int, q: int, num_splits
         else:     # workgroup i on XCD i mod n_xcd
             for t in range(m_tiles):
                 queues[(g * m_tiles + t) % n_xcd].append(cost[split])
+    if bf16 and num_splits == 1 and cut_applies(queues, cu_per_xcd):
+        # the library's last-round cut: units after an XCD's whole rounds run as pieces
+        for i, queue in enumerate(queues):
+            whole = len(queue) // cu_per_xcd * cu_per_xcd
+            left = len(queue) - whole
+            if left and cu_per_xcd // left >= 2:
+                k = cu_per_xcd // left
+                piece = math.ceil((prefix + q) / 32 / k) * 32 + overhead_keys
+                queues[i] = queue[:whole] + [piece] * (left * k)
     worst = 0.0
     for queue in queues:
         cus = [0.0] * cu_per_xcd
@@ -338,6 +347,15 @@ def _schedule_makespan(batch: int, m_tiles: int, prefix: int, q: int, num_splits
             heapq.heappush(cus, heapq.heappop(cus) + c)
         worst = max(worst, max(cus))
     return worst
+
+
+def cut_applies(queues, cu_per_xcd: int = 32, max_rounds: int = 2) -> bool:
+    # the library's rule for the last-round cut of a one-split bf16 launch: every XCD's
+    # queue has at most max_rounds whole rounds, and some XCD has units left over that
+    # can be cut into at least two pieces each
+    if any(len(qu) // cu_per_xcd > max_rounds for qu in queues):
+        return False
+    return any(0 < len(qu) % cu_per_xcd <= cu_per_xcd // 2 for qu in queues)
 
 
 def choose_split_ratio(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
@@ -377,7 +395,8 @@ def choose_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
     cheapest pair, fewer splits on ties.  Its picks matched the fastest of those timed on
     MI355X for 4 requests with 65-node trees and 64 heads: 4 splits at ratio 0.75 for
     4096-key prefixes (0.251 ms; 3 equal splits 0.301 ms), 8 at 0.75 for 32768-key ones
-    (1.148 ms; 16 at 0.85 1.247 ms); 2 at 0.4 for 8 requests of 4096 keys."""
+    (1.148 ms; 16 at 0.85 1.247 ms); for 8 requests of 4096 keys, 1 split with the
+    library's last-round cut (0.317 ms; 2 splits at 0.4 0.388 ms)."""
     m_tiles = math.ceil(max_q_len * num_heads / 128)
     prefix = max(0, int(round(mean_kv)) - max_q_len)
     rows = batch * max_q_len * num_heads
@@ -400,6 +419,12 @@ def choose_splits(batch: int, num_heads: int, max_q_len: int, mean_kv: float,
         t = span * us_per_key
         if s > 1:
             t += (s + 1) * rows * (DL_BYTES + 4) / (merge_gbs * 1e3) + merge_fixed_us
+        else:  # the last-round cut's piece merge, when the library applies it
+            queues = [[0] * (m_tiles * (batch // n_xcd + (x < batch % n_xcd)))
+                      for x in range(n_xcd)]
+            if cut_applies(queues, cu_per_xcd):
+                cut_rows = sum(len(qu) % cu_per_xcd for qu in queues) * 128
+                t += cu_per_xcd * cut_rows * (DL_BYTES + 4) / (merge_gbs * 1e3) + merge_fixed_us
         if best is None or t < best[0]:
             best = (t, s, r)
         if (prefix + s - 1) // s <= 32:
@@ -465,6 +490,11 @@ class VerifyAttn:
         dt = KDTREE_DTYPE_BF16 if dtype == torch.bfloat16 else KDTREE_DTYPE_FP32
         need = kdtree_verify_attn_workspace_bytes(total_q, total_kv, batch, h, int(num_splits), dt)
         if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            if phase != "all" and workspace is not None:
+                # the two halves must share the caller's buffer: a new one would hold no
+                # pre-pass output
+                raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} "
+                                 f"bytes, {need} needed for num_splits={num_splits}")
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_ptr = workspace.data_ptr() if (workspace is not None and need) else 0
         ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0

@@ -27,6 +27,7 @@ namespace kdt {
 namespace {
 
 constexpr int BM = 128;     // query rows per workgroup
+static_assert(BM == PIECE_ROWS, "cut pieces hold one row tile");
 constexpr int BN = 32;      // keys per tile
 constexpr int NTHR = 256;   // 4 waves
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
@@ -494,8 +495,27 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   // the pre-pass) then split, and dealt to the XCDs in snake order (ranks 0..7 to XCDs
   // 0..7, ranks 8..15 to XCDs 7..0, ...), so every XCD gets an even, longest-first share
   // of the work, and the row tiles of a group share that XCD's L2.
-  const int slot = blockIdx.x / NUM_XCD;
+  int slot = blockIdx.x / NUM_XCD;
   const int xcd = (int)(blockIdx.x % NUM_XCD);
+  // Last-round cut (one split): the units of this XCD's queue after its whole rounds of
+  // CUS_PER_XCD are skipped here and run instead as key pieces, workgroups appended to
+  // the grid (blockIdx = NUM_XCD * (normal_slots + j) + xcd, piece j of this XCD).
+  int piece = -1, pieces = 0, pslot = 0, punit = 0;
+  if (p.cut) {
+    const int normal_slots = ((p.batch + NUM_XCD - 1) / NUM_XCD) * p.m_tiles;
+    const XcdCut cut = xcd_cut(p.batch, p.m_tiles, xcd);
+    if (slot >= normal_slots) {
+      const int j = slot - normal_slots;
+      if (j >= cut.left * cut.pieces) return;
+      pieces = cut.pieces;
+      punit = j / pieces;
+      piece = j % pieces;
+      pslot = xcd * CUS_PER_XCD + j;
+      slot = cut.whole + punit;
+    } else if (cut.left && slot >= cut.whole) {
+      return;
+    }
+  }
   const int round = slot / p.m_tiles;
   const int grank = NUM_XCD * round + ((round & 1) ? NUM_XCD - 1 - xcd : xcd);
   if (grank >= p.batch * p.num_splits) return;
@@ -582,12 +602,33 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
     x = sParent[x];
   }
 
-  // ---- key range of this split ---------------------------------------------------
+  // ---- key range of this split (or piece) --------------------------------------------
   const int S = p.num_splits;
   // whole 32-key tiles, so every split starts on a V^T tile boundary
-  int k_begin = split_begin(P, S, p.split_ratio, split);
-  const int k_end = (split == S - 1) ? P + T : split_begin(P, S, p.split_ratio, split + 1);
+  int k_begin, k_end;
+  if (piece < 0) {
+    k_begin = split_begin(P, S, p.split_ratio, split);
+    k_end = (split == S - 1) ? P + T : split_begin(P, S, p.split_ratio, split + 1);
+  } else {  // one split: piece `piece` of `pieces` equal runs of whole tiles
+    const int per = ((P + T + BN - 1) / BN + pieces - 1) / pieces;
+    k_begin = min(piece * per * BN, P + T);
+    k_end = min((piece + 1) * per * BN, P + T);
+    if (piece == 0 && tid == 0) {  // where the piece merge writes this unit's rows
+      p.piece_desc[2 * (xcd * CUS_PER_XCD + punit)] = qoff * H + m0;
+      p.piece_desc[2 * (xcd * CUS_PER_XCD + punit) + 1] = min(BM, rows - m0);
+    }
+  }
   const int64_t grow = qoff * H + crow;  // global query row
+  if (piece >= 0 && k_end <= k_begin) {
+    // empty piece: partial = (0, -inf)
+    if (row_ok) {
+      const int64_t prow = (int64_t)pslot * BM + (row - m0);
+      float* po = p.piece_o + prow * DL;
+      for (int f = h * 4; f < DL; f += 8) *(float4*)(po + f) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (h == 0) p.piece_lse[prow] = -INFINITY;
+    }
+    return;
+  }
   if (k_end <= k_begin) {
     // empty split: partial = (0, -inf)
     if (row_ok) {
@@ -675,14 +716,17 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
 
   // ---- finalize -------------------------------------------------------------------
   const float l_tot = pair_sum(st.l);
-  const float inv = 1.0f / l_tot;
-  const float lse = st.m * LN2 + logf(l_tot);
+  // A cut piece may hold only tree-tail keys that a row cannot see: its partial is then
+  // (0, -inf), as for an empty split.  (A whole split always holds the node itself.)
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse = l_tot > 0.0f ? st.m * LN2 + logf(l_tot) : -INFINITY;
   // A wave's 32 rows are consecutive global rows, so its output block is contiguous.
   const int wrow0 = m0 + wave * 32;
   const int wrows = min(32, rows - wrow0);  // rows of this wave that exist (may be <= 0)
   const int64_t gbase = qoff * H + wrow0;
-  float* const out = S == 1 ? p.out_lat + gbase * DL
-                             : p.part_o + ((int64_t)split * p.total_q * H + gbase) * DL;
+  float* const out = piece >= 0 ? p.piece_o + ((int64_t)pslot * BM + wave * 32) * DL
+                   : S == 1    ? p.out_lat + gbase * DL
+                               : p.part_o + ((int64_t)split * p.total_q * H + gbase) * DL;
   // The accumulator layout gives each lane 16-byte pieces of one row, so direct stores
   // would touch 32 rows per instruction.  Instead each wave passes its block through LDS
   // (the tile ring, free once every wave has finished the last tile), 128 features at a
@@ -727,11 +771,16 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   // last, so that no global store is outstanding when the first LDS write above waits
   // for the tile copies
   if (row_ok && h == 0) {
-    if (S == 1)
+    if (piece >= 0)
+      p.piece_lse[(int64_t)pslot * BM + (row - m0)] = lse;
+    else if (S == 1)
       p.out_lse[grow] = lse;
     else
       p.part_lse[(int64_t)split * p.total_q * H + grow] = lse;
-    if (!(fabsf(lse) < INFINITY) && p.status) atomicOr(p.status, ST_NONFINITE);
+    // a piece's lse may be -inf (no visible key); NaN still means non-finite data, and
+    // the piece merge leaves such rows unwritten
+    if ((piece < 0 ? !(fabsf(lse) < INFINITY) : __builtin_isnan(lse)) && p.status)
+      atomicOr(p.status, ST_NONFINITE);
   }
 }
 
@@ -741,7 +790,10 @@ int rows_per_block_bf16() { return BM; }
 
 hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream) {
   const int64_t groups = (int64_t)p.batch * p.num_splits;
-  const int64_t blocks = (int64_t)NUM_XCD * ((groups + NUM_XCD - 1) / NUM_XCD) * p.m_tiles;
+  if (p.cut && (p.num_splits != 1 || !p.piece_o || !p.piece_lse || !p.piece_desc))
+    return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)NUM_XCD * ((groups + NUM_XCD - 1) / NUM_XCD) * p.m_tiles +
+                         (p.cut ? PIECE_SLOTS : 0);
   if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(verify_attn_bf16_kernel, dim3((unsigned)blocks), dim3(NTHR), 0, stream, p);
   return hipGetLastError();

@@ -4,22 +4,27 @@
 // the kernels on the caller's stream.
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/kdtree_verify.h"
+
 #include "common.h"
 
 namespace {
 
 constexpr int32_t kMaxSplits = kdt::MAX_SPLITS;
+constexpr int kCutMaxRounds = 2;  // cut only when every XCD's queue has at most 2 whole rounds
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t order_bytes, k16_bytes, part_o_bytes, part_lse_bytes, total;
+  size_t order_bytes, k16_bytes, part_o_bytes, part_lse_bytes, piece_bytes, total;
   int64_t k16_tiles;
 };
 
-// Workspace: [request order + fp16 latent tiles (bf16 inputs)] [split partial outputs]
-// [split lse], each region 256-byte aligned.  Latent tiles: one 32 KB tile per 32 keys
+// Workspace: [request order + fp16 latent tiles (bf16 inputs)] [split partial outputs +
+// split lse, or (bf16, one split) the last-round cut pieces], each region 256-byte
+// aligned.  Latent tiles: one 32 KB tile per 32 keys
 // of every request, bounded by total_kv / 32 + batch (each request adds at most one
 // partial tile).
 bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t num_heads,
@@ -34,7 +39,15 @@ bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t 
   const size_t rows = (size_t)total_q * (size_t)num_heads;
   w->part_o_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * kdt::DL * sizeof(float), 256) : 0;
   w->part_lse_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * sizeof(float), 256) : 0;
-  w->total = w->order_bytes + w->k16_bytes + w->part_o_bytes + w->part_lse_bytes;
+  // Last-round cut pieces (bf16, one split): outputs, lse, and two int64 per unit.  They
+  // share one region with the split partials (a launch uses one or the other), sized for
+  // the larger, so a workspace sized for more splits also serves fewer.
+  w->piece_bytes = dtype == KDTREE_DTYPE_BF16
+                       ? (size_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS * (kdt::DL + 1) * sizeof(float) +
+                             (size_t)kdt::PIECE_SLOTS * 2 * sizeof(int64_t)
+                       : 0;
+  const size_t shared = std::max(w->part_o_bytes + w->part_lse_bytes, w->piece_bytes);
+  w->total = w->order_bytes + w->k16_bytes + shared;
   return true;
 }
 
@@ -79,6 +92,14 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
   p.part_o = num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes) : nullptr;
   p.part_lse =
       num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes + w.part_o_bytes) : nullptr;
+  char* pw = ws + w.order_bytes + w.k16_bytes;  // the region shared with the partials
+  const bool pieces = w.piece_bytes && num_splits == 1;
+  p.piece_o = pieces ? (float*)pw : nullptr;
+  p.piece_lse = pieces ? (float*)pw + (size_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS * kdt::DL
+                       : nullptr;
+  p.piece_desc = pieces ? (int64_t*)(pw + (size_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS *
+                                              (kdt::DL + 1) * sizeof(float))
+                        : nullptr;
   p.status = status;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.split_ratio = split_ratio;
@@ -91,6 +112,17 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
   const int bm = dtype == KDTREE_DTYPE_BF16 ? kdt::rows_per_block_bf16() : kdt::rows_per_block_f32();
   p.m_tiles = (max_q_len * num_heads + bm - 1) / bm;
   if ((int64_t)p.m_tiles * num_splits * batch > 0x7fffffff) return KDTREE_ERR_SHAPE;
+  // Cut the last, partly filled round of each XCD's queue into key pieces when whole
+  // rounds are few (there the leftover round is a large share of the launch); with more
+  // rounds the longest-first order already fills it.
+  p.cut = 0;
+  if (pieces) {
+    for (int x = 0; x < kdt::NUM_XCD; ++x) {
+      const kdt::XcdCut c = kdt::xcd_cut(batch, p.m_tiles, x);
+      if (c.whole > kCutMaxRounds * kdt::CUS_PER_XCD) { p.cut = 0; break; }
+      if (c.left) p.cut = 1;
+    }
+  }
   return KDTREE_OK;
 }
 
@@ -108,8 +140,17 @@ int32_t launch_attend(const kdt::VerifyParams& p, int32_t dtype, hipStream_t s) 
     e = kdt::launch_fill_nan(p.part_lse, (int64_t)p.num_splits * p.total_q * p.num_heads, s);
     if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
   }
+  if (p.cut) {
+    // piece lse = NaN until a piece writes it: the piece merge leaves rows no piece wrote
+    e = kdt::launch_fill_nan(p.piece_lse, (int64_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS, s);
+    if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
+  }
   e = dtype == KDTREE_DTYPE_BF16 ? kdt::launch_verify_bf16(p, s) : kdt::launch_verify_f32(p, s);
   if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
+  if (p.cut) {
+    e = kdt::launch_piece_merge(p, s);
+    if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
+  }
   if (p.num_splits > 1) {
     e = kdt::launch_lse_merge(p.part_o, p.part_lse, p.out_lat, p.out_lse,
                               p.total_q * p.num_heads, p.num_splits, s);

@@ -15,6 +15,9 @@ constexpr int TILE_KEYS = 32;              // keys per pre-converted fp16 latent
 constexpr int64_t TILE_BYTES = DL * TILE_KEYS * 2;
 constexpr int ORDER_MAX_BATCH = 4096;      // larger batches keep the request order as given
 constexpr int NUM_XCD = 8;                 // MI355X: workgroup i runs on XCD i % 8
+constexpr int CUS_PER_XCD = 32;
+constexpr int PIECE_SLOTS = NUM_XCD * CUS_PER_XCD;  // cut pieces per launch, at most
+constexpr int PIECE_ROWS = 128;                     // rows of one bf16 row tile
 constexpr int MAX_SPLITS = 256;            // split-KV factor limit
 constexpr float LN2 = 0.69314718055994530942f;
 
@@ -42,6 +45,12 @@ struct VerifyParams {
   int32_t batch, num_heads, max_q_len, num_splits, m_tiles;
   int64_t total_q, total_kv;
   int64_t k16_tiles; // capacity of `k16` in tiles
+  // Last-round cut (bf16, one split): each XCD's units after its whole rounds of
+  // CUS_PER_XCD run as key pieces, written here and merged by launch_piece_merge.
+  int32_t cut;         // 0: off
+  float* piece_o;      // [NUM_XCD * CUS_PER_XCD pieces, 128 rows, 512]
+  float* piece_lse;    // [NUM_XCD * CUS_PER_XCD pieces, 128 rows]
+  int64_t* piece_desc; // [NUM_XCD * CUS_PER_XCD units] x {first global row, rows}
 };
 
 // Draft-tree builder and accept.
@@ -116,6 +125,25 @@ __device__ __forceinline__ int split_begin(int P, int S, float r, int s) {
   return (int)(b < P ? b : P);
 }
 
+// Last-round cut of one XCD's queue (bf16 kernel, one split).  The kernel deals groups
+// of m_tiles row tiles to the XCDs in snake order; XCD x's queue then holds n units, the
+// first `whole` of them in whole rounds of CUS_PER_XCD.  Each of the `left` units after
+// them is cut into `pieces` key pieces (0 when there is nothing to cut).
+struct XcdCut {
+  int whole, left, pieces;
+};
+__host__ __device__ inline XcdCut xcd_cut(int groups, int m_tiles, int xcd) {
+  const int full_rounds = groups / NUM_XCD, rem = groups % NUM_XCD;
+  const int pos = (full_rounds & 1) ? NUM_XCD - 1 - xcd : xcd;  // in the partial round
+  const int n = (full_rounds + (pos < rem ? 1 : 0)) * m_tiles;
+  XcdCut c;
+  c.whole = n / CUS_PER_XCD * CUS_PER_XCD;
+  c.left = n - c.whole;
+  c.pieces = c.left ? CUS_PER_XCD / c.left : 0;
+  if (c.pieces < 2) c.left = c.pieces = 0;
+  return c;
+}
+
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_sample_tokens(const SampleParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_pack_tree(const PackParams& p, hipStream_t stream);
@@ -127,6 +155,7 @@ hipError_t launch_prepass(const VerifyParams& p, int64_t n_tiles_bound, hipStrea
 hipError_t launch_fill_nan(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, float* out_lat,
                             float* out_lse, int64_t rows, int32_t num_splits, hipStream_t stream);
+hipError_t launch_piece_merge(const VerifyParams& p, hipStream_t stream);
 int rows_per_block_bf16();
 int rows_per_block_f32();
 

@@ -103,7 +103,69 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   if (lane == 0) out_lse[row] = wsum > 0.0f ? big + logf(wsum) : -INFINITY;
 }
 
+// Piece merge of the last-round cut: one wavefront per (XCD, cut unit, row).  Lane k < K
+// holds the lse of piece k; the same weights as above combine the K pieces' outputs into
+// the unit's output row (the pieces cover the request's whole key range).  A row whose
+// piece lse is still NaN in some piece was not computed (a skipped request, or a row past
+// the request's rows) and is left unwritten.
+__global__ __launch_bounds__(256) void piece_merge_kernel(const float* __restrict__ piece_o,
+                                                          const float* __restrict__ piece_lse,
+                                                          const int64_t* __restrict__ desc,
+                                                          float* __restrict__ out_lat,
+                                                          float* __restrict__ out_lse,
+                                                          int32_t* __restrict__ status,
+                                                          int groups, int m_tiles,
+                                                          int64_t total_rows) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * MERGE_ROWS + (threadIdx.x >> 6);  // (xcd, unit, row)
+  const int row = w % PIECE_ROWS;
+  const int unit = (w / PIECE_ROWS) % CUS_PER_XCD;
+  const int xcd = w / (PIECE_ROWS * CUS_PER_XCD);
+  if (xcd >= NUM_XCD) return;
+  const XcdCut cut = xcd_cut(groups, m_tiles, xcd);
+  if (unit >= cut.left) return;
+  const int k_n = cut.pieces;  // 2..32
+  const int64_t s0 = (int64_t)xcd * CUS_PER_XCD + (int64_t)unit * k_n;  // first piece slot
+  const float ls = lane < k_n ? piece_lse[(s0 + lane) * PIECE_ROWS + row] : -INFINITY;
+  if (__builtin_amdgcn_ballot_w64(__builtin_isnan(ls))) return;
+  const int64_t d = (int64_t)xcd * CUS_PER_XCD + unit;
+  const int64_t grow = desc[2 * d] + row;
+  if (row >= desc[2 * d + 1] || desc[2 * d] < 0 || grow >= total_rows) return;
+  const float big = wave_max_f(ls);
+  const float bref = big == -INFINITY ? 0.0f : big;
+  const float wl = ls == -INFINITY ? 0.0f : __expf(ls - bref);
+  const float wsum = wave_sum_f(wl);
+  const float* src = piece_o + (s0 * PIECE_ROWS + row) * DL + lane * 4;
+  float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+  for (int k = 0; k < k_n; ++k) {
+    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+    const float4 v0 = *(const float4*)(src + (int64_t)k * PIECE_ROWS * DL);
+    const float4 v1 = *(const float4*)(src + (int64_t)k * PIECE_ROWS * DL + 256);
+    a0.x += wk * v0.x; a0.y += wk * v0.y; a0.z += wk * v0.z; a0.w += wk * v0.w;
+    a1.x += wk * v1.x; a1.y += wk * v1.y; a1.z += wk * v1.z; a1.w += wk * v1.w;
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  float* dst = out_lat + grow * DL + lane * 4;
+  *(float4*)dst = make_float4(a0.x * inv, a0.y * inv, a0.z * inv, a0.w * inv);
+  *(float4*)(dst + 256) = make_float4(a1.x * inv, a1.y * inv, a1.z * inv, a1.w * inv);
+  if (lane == 0) {
+    const float lse = wsum > 0.0f ? big + logf(wsum) : -INFINITY;
+    out_lse[grow] = lse;
+    if (!(fabsf(lse) < INFINITY) && status) atomicOr(status, ST_NONFINITE);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_piece_merge(const VerifyParams& p, hipStream_t stream) {
+  if (!p.cut) return hipSuccess;
+  const int blocks = PIECE_SLOTS * PIECE_ROWS / MERGE_ROWS;
+  hipLaunchKernelGGL(piece_merge_kernel, dim3(blocks), dim3(256), 0, stream, p.piece_o,
+                     p.piece_lse, p.piece_desc, p.out_lat, p.out_lse, p.status, p.batch,
+                     p.m_tiles,
+                     p.total_q * p.num_heads);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_nan(float* p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;

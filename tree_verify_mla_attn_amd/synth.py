@@ -246,15 +246,17 @@ def make_inputs(rng: np.random.Generator, *, num_heads: int, prefix_lens: Sequen
 # launch configuration (workload 5 prescribes 16 chunks; the others use the count that
 # ran fastest on MI355X: small fp32 batches need splits to occupy the chip, and the best
 # counts keep the workgroups (row tiles x splits) within one round of the 256 CUs).  Where
-# the workgroups overrun whole rounds of the CUs (workload 3: 528 on 256; workload 5:
-# 2112), geometric chunk sizes (split_ratio < 1, largest first) ran fastest in sweeps.
+# the workgroups overrun whole rounds of the CUs, workload 5 (2112 workgroups) runs
+# fastest with geometric chunk sizes (split_ratio < 1, largest first), and workload 3
+# (264 row tiles on 256 CUs) with one split, its 33rd row tile per XCD cut into key
+# pieces by the library (faster than 2 geometric splits at ratio 0.4).
 CONFIGS = {
     1: dict(name="tiny_b1_p256_q9_fp32", batch=1, heads=64, prefix=256, top_k=[8], budget=8,
             dtype="fp32", num_splits=12),
     2: dict(name="b1_p2048_q33_wide_fp32", batch=1, heads=64, prefix=2048, top_k=[8], budget=32,
             dtype="fp32", num_splits=7),
     3: dict(name="b8_p4096_q65_deep_bf16", batch=8, heads=64, prefix=4096, top_k=[2], budget=64,
-            dtype="bf16", num_splits=2, split_ratio=0.4),
+            dtype="bf16", num_splits=1),
     4: dict(name="b64_ragged1024-8192_q33_mixed_bf16", batch=64, heads=64, prefix=(1024, 8192),
             top_k=[8] * 32 + [2] * 32, budget=32, dtype="bf16", num_splits=1),
     5: dict(name="b4_p32768_q65_split16_bf16", batch=4, heads=64, prefix=32768, top_k=[4],
