@@ -449,6 +449,13 @@ def main():
     measured = measured_peaks(torch, dev) if args.measure_peaks else None
 
     dtype = inp.dtype
+    bf16_id = B.KDTREE_DTYPE_BF16 if dtype == "bf16" else B.KDTREE_DTYPE_FP32
+    if splits > 1:
+        kernel_label = "attention + merge"
+    elif B.launch_uses_cut(inp.batch, inp.num_heads, inp.max_q_len, splits, bf16_id):
+        kernel_label = "attention + piece merge"
+    else:
+        kernel_label = "attention"
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
@@ -472,7 +479,7 @@ def main():
                    "q_len": int(inp.max_q_len), "total_q": inp.total_q, "total_kv": inp.total_kv,
                    "num_splits": splits, "split_ratio": ratio, "d_latent": 512, "d_rope": 64,
                    "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
-        "roofline": {"bound": "mfma", "kernel": "attention" + (" + merge" if splits > 1 else ""),
+        "roofline": {"bound": "mfma", "kernel": kernel_label,
                      "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic["bytes"] if traffic else None},

@@ -82,6 +82,13 @@ extern "C" {
 #define KDTREE_STATUS_NONFINITE 16u   /* a non-finite output row was produced (with the
                                          bf16 last-round cut, such a row of a cut row
                                          tile may be left unwritten instead) */
+#define KDTREE_STATUS_RANGE 32u       /* bf16 inputs: a q_lat or kv_lat value is not
+                                         finite or has |x| >= 65504, outside the fp16
+                                         range of the latent contractions.  The call
+                                         still completes; the rows of the affected
+                                         request (every row that sees such a key, or
+                                         whose query holds such a value) are then
+                                         meaningless, typically inf or NaN. */
 
 /* MAX_QLEN (65). */
 int32_t kdtree_max_qlen(void);
@@ -111,7 +118,7 @@ size_t kdtree_verify_attn_workspace_bytes(int64_t total_q, int64_t total_kv, int
  *       bf16 contract: values must be finite with |x| < 65504 in q_lat and kv_lat
  *       (the latent contractions run as fp16 MFMAs with fp32 accumulation; bf16 ->
  *       fp16 is exact for 2^-17 <= |x| < 65504, smaller magnitudes round with an
- *       absolute error <= 2^-25).
+ *       absolute error <= 2^-25).  A value outside it sets KDTREE_STATUS_RANGE.
  *   prefix_len, tree_parent, q_len  device int32 arrays (layout above).
  *   scale        softmax scale applied to q . k (finite; e.g. 1/sqrt(192)).
  *   out_lat      device fp32 [total_q, H, 512];  out_lse device fp32 [total_q, H].

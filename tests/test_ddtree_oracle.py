@@ -254,3 +254,26 @@ def test_planted_builder_mistakes_fail(old, new):
 ])
 def test_planted_accept_mistakes_fail(old, new):
     assert not _accept_pins_pass(_mutant(old, new))
+
+
+# ------------------------------------------------------------------ batch helper
+@pytest.mark.parametrize("budget", [0, 5, 32, 64])
+def test_batch_helper_pads_per_request_trees(budget):
+    """build_ddtree_batch = build_ddtree per request, written into rows of width
+    budget + 1 with -1 past each tree, and q_len = the tree's node count."""
+    rng = np.random.default_rng(700 + budget)
+    logp, ids, root = synth.draft_tables(rng, 5, [8, 2, 4, 1, 3], depth=15, vocab=512)
+    logp[4, 3:, :] = -np.inf  # a request whose table ends at depth 3 (underfull tree)
+    got = D.build_ddtree_batch(logp, ids, root, budget)
+    assert got["q_len"].shape == (5,)
+    for b in range(5):
+        t = D.build_ddtree(logp[b], ids[b], int(root[b]), budget)
+        n = len(t["parent"])
+        assert got["q_len"][b] == n
+        for k in ("parent", "token", "depth", "first_child", "next_sibling"):
+            row = got[k][b]
+            assert row.shape == (budget + 1,) and row.dtype == np.int32
+            np.testing.assert_array_equal(row[:n], t[k], err_msg=f"{k} b={b}")
+            assert (row[n:] == -1).all(), f"{k} b={b} padding"
+    # the underfull request (top-3 over 3 depths) has 3 + 9 + 27 candidate paths
+    assert got["q_len"][4] == min(budget, 3 + 9 + 27) + 1

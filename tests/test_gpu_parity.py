@@ -2,15 +2,14 @@
 
 Bars: fp32 inputs -> max |gpu - oracle| <= 1e-5 on out_lat and out_lse; bf16 inputs ->
 |gpu - oracle| <= 1e-3 + 2e-3 |oracle| elementwise, oracle fed the same bf16 values.
-Small cases compare every element; the large workloads (batch 8 / 64 / 4 at H=64) run in
-the launch configuration the benchmark times and compare sampled rows that the oracle
-computes one by one, plus whole-output properties.
+Every case compares every element, the large workloads (batch 8 / 64 / 4 at H=64) too, in
+the launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
 import torch
 
-from oracle import verify_attn_inputs, verify_attn_rows
+from oracle import verify_attn_inputs
 from tree_verify_mla_attn_amd import binding as B
 from tree_verify_mla_attn_amd import synth
 
@@ -133,46 +132,149 @@ def test_small_workloads_full(dev, cfg):
                split_ratio=inp.split_ratio)
 
 
-def _sample_rows(inp, rng, per_request_nodes=3, heads=(0, 63)):
-    picks = []
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_large_workloads_full(dev, cfg):
+    """Every element of the batch-8 / batch-64 / batch-4 workloads, in the launch
+    configuration the benchmark times (workload 3 and 4: one split, workload 3 through the
+    last-round cut; workload 5: 16 geometric splits at ratio 0.85), against the full
+    float64 oracle on the same bf16 values."""
+    inp = synth.config_inputs(cfg)
+    full_check(f"workload{cfg}", inp, dev, num_splits=inp.num_splits,
+               split_ratio=inp.split_ratio)
+
+
+def test_workload4_metamorphic(dev):
+    """Full-size checks that sampling cannot miss, on the batch-64 workload:
+    * one tail key row per request (the last tree node's, a leaf) is replaced by new
+      values; every row of a node that does not see that key is bit-identical, and the
+      rows that do see it change;
+    * reversing the head order of the queries reverses the heads of the outputs, bit for
+      bit (every row is computed on its own)."""
+    inp = synth.config_inputs(4)
+    out, lse, st = run(inp, dev)
+    assert st == 0
+    out, lse = out.cpu(), lse.cpu()
+    rng = np.random.default_rng(4004)
+    kv_lat, k_rope = inp.kv_lat.copy(), inp.k_rope.copy()
+    qo, ko = inp.q_offsets(), inp.kv_offsets()
+    sees = np.zeros(inp.total_q, bool)
     for b in range(inp.batch):
         par = inp.parents_of(b)
-        dep = synth.tree_depths(par)
-        nodes = {0, len(par) - 1, int(np.argmax(dep))}
-        nodes |= set(int(x) for x in rng.integers(0, len(par), per_request_nodes))
-        hs = set(heads) | set(int(x) for x in rng.integers(0, inp.num_heads, 2))
-        picks.append((b, sorted(nodes), sorted(hs)))
-    return picks
+        j = len(par) - 1
+        row = ko[b] + int(inp.prefix_len[b]) + j
+        kv_lat[row] = synth.round_to_bf16(rng.standard_normal(512).astype(np.float32) * 3)
+        k_rope[row] = synth.round_to_bf16(rng.standard_normal(64).astype(np.float32) * 3)
+        for i in range(len(par)):
+            x = i
+            while x != -1 and x != j:
+                x = int(par[x])
+            sees[qo[b] + i] = x == j
+    pert = synth.VerifyInputs(**{**inp.__dict__, "kv_lat": kv_lat, "k_rope": k_rope})
+    out2, lse2, st = run(pert, dev)
+    assert st == 0
+    out2, lse2 = out2.cpu(), lse2.cpu()
+    keep = torch.from_numpy(~sees)
+    print(f"rows seeing a perturbed key: {int(sees.sum())} of {inp.total_q}", flush=True)
+    assert torch.equal(out2[keep], out[keep]) and torch.equal(lse2[keep], lse[keep])
+    # rows that see the new key move (a row whose old and new scores are both tiny could
+    # in principle stay the same in fp32, so this asks for nearly all of them)
+    seen = torch.from_numpy(sees)
+    moved = (out2[seen] != out[seen]).any(dim=2)
+    assert moved.float().mean().item() > 0.99, moved.float().mean().item()
+    flip = synth.VerifyInputs(**{**inp.__dict__, "q_lat": inp.q_lat[:, ::-1].copy(),
+                                 "q_rope": inp.q_rope[:, ::-1].copy()})
+    out3, lse3, st = run(flip, dev)
+    assert st == 0
+    assert torch.equal(out3.cpu(), out.flip(1)) and torch.equal(lse3.cpu(), lse.flip(1))
 
 
-@pytest.mark.parametrize("cfg", [3, 4, 5])
-def test_large_workloads_sampled(dev, cfg):
-    inp = synth.config_inputs(cfg)
-    splits = inp.num_splits
-    print(f"case workload{cfg} splits={splits} ratio={inp.split_ratio}", flush=True)
-    out, lse, st = run(inp, dev, splits, split_ratio=inp.split_ratio)
-    assert st == 0, B.decode_status(st)
-    out_np = out.cpu().numpy()
-    lse_np = lse.cpu().numpy()
-    assert np.isfinite(out_np).all() and np.isfinite(lse_np).all()
-    assert np.abs(out_np).max() <= np.abs(inp.kv_lat).max() + 1e-3  # convex combination
-    qo = inp.q_offsets()
-    rng = np.random.default_rng(cfg)
-    picks = _sample_rows(inp, rng, per_request_nodes=2 if cfg == 4 else 4)
-    g_o, g_l, r_o, r_l = [], [], [], []
-    for b, nodes, hs in picks:
-        ro, rl = verify_attn_rows(inp, b, nodes, hs)
-        rows = qo[b] + np.asarray(nodes)
-        g_o.append(out_np[rows][:, hs])
-        g_l.append(lse_np[rows][:, hs])
-        r_o.append(ro)
-        r_l.append(rl)
-    check(f"workload{cfg} sampled", inp, np.concatenate([x.reshape(-1, 512) for x in g_o]),
-          np.concatenate([x.ravel() for x in g_l]),
-          np.concatenate([x.reshape(-1, 512) for x in r_o]), np.concatenate([x.ravel() for x in r_l]))
+def test_one_split_without_cut_several_rounds(dev):
+    """The uncut one-split path with more than two whole rounds of row tiles per XCD (24
+    requests x 33 row tiles at q_len 65 and 64 heads), every element."""
+    rng = np.random.default_rng(90)
+    parents = [synth.random_tree(rng, 65) for _ in range(24)]
+    prefix = rng.integers(0, 200, size=24)
+    inp = synth.make_inputs(rng, num_heads=64, prefix_lens=prefix, parents=parents,
+                            dtype="bf16")
+    full_check("uncut24", inp, dev)
+
+
+@pytest.mark.parametrize("case", [c for c in EDGE])
+def test_edge_cases_bf16_cut_off(dev, case, monkeypatch):
+    """The bf16 edge cases again with the last-round cut switched off, so that the uncut
+    one-split path is covered on each of them (most small launches are cut)."""
+    monkeypatch.setenv("KDTREE_DISABLE_CUT", "1")
+    full_check(f"{case}/bf16/nocut", EDGE[case]("bf16"), dev)
 
 
 # ------------------------------------------------------------------ robustness
+def test_bf16_range_status(dev):
+    """A bf16 latent value outside fp16's range (|x| >= 65504, or not finite) sets the
+    range bit, in kv_lat (seen by the pre-pass) and in q_lat (seen by the Q load); the
+    largest bf16 value below 65504 does not."""
+    base = EDGE["ragged_batch5_h64"]("bf16")
+    cases = []
+    kv = base.kv_lat.copy()
+    kv[40, 17] = 65280.0          # largest bf16 below 65504: in range
+    cases.append(("in_range", dict(kv_lat=kv), 0))
+    kv = base.kv_lat.copy()
+    kv[40, 17] = 1.0e5
+    cases.append(("kv_big", dict(kv_lat=kv), 32))
+    kv = base.kv_lat.copy()
+    kv[-1, 3] = -np.inf
+    cases.append(("kv_inf", dict(kv_lat=kv), 32))
+    q = base.q_lat.copy()
+    q[7, 5, 100] = -7.0e4
+    cases.append(("q_big", dict(q_lat=q), 32))
+    for name, change, bit in cases:
+        inp = synth.VerifyInputs(**{**base.__dict__, **change})
+        print(f"case range/{name}", flush=True)
+        _, _, st = run(inp, dev)
+        print(f"range/{name}: status {st} {B.decode_status(st)}", flush=True)
+        assert (st & 32) == bit, name
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_requests_before_a_malformed_one_are_computed(dev, splits):
+    """q_len[2] = 0: requests 2.. are skipped and flagged, requests 0 and 1 are computed
+    (their fp16 tiles converted by the pre-pass) and match the oracle."""
+    base = EDGE["ragged_batch5_h64"]("bf16")
+    bad_q = base.q_len.copy()
+    bad_q[2] = 0
+    inp = synth.VerifyInputs(**{**base.__dict__, "q_len": bad_q})
+    d = synth.device_tensors(inp, dev)
+    h = inp.num_heads
+    n01 = int(base.q_len[0] + base.q_len[1])
+    rows = base.total_q  # the packed rows the caller allocated (q_len no longer sums to it)
+    out = torch.full((rows, h, 512), 7.25, dtype=torch.float32, device=dev)
+    lse = torch.full((rows, h), 7.25, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    print(f"case malformed_q2 splits={splits}", flush=True)
+    B.verify_attn(d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"],
+                  d["tree_parent"], d["q_len"], inp.scale, out_lat=out, out_lse=lse,
+                  num_splits=splits, max_q_len=65, status=status)
+    torch.cuda.synchronize(dev)
+    assert int(status.item()) & 1
+    assert (out[n01:] == 7.25).all() and (lse[n01:] == 7.25).all()
+    first = synth.VerifyInputs(**{**base.__dict__, "q_len": base.q_len[:2].copy(),
+                                  "prefix_len": base.prefix_len[:2].copy(),
+                                  "tree_parent": base.tree_parent[:n01].copy(),
+                                  "q_lat": base.q_lat[:n01], "q_rope": base.q_rope[:n01]})
+    r_out, r_lse = verify_attn_inputs(first)
+    check(f"malformed_q2/{splits}", first, out[:n01].double().cpu().numpy(),
+          lse[:n01].double().cpu().numpy(), r_out, r_lse)
+
+
+def test_phase_calls_need_the_callers_workspace(dev):
+    inp = EDGE["chain9_p37_h64"]("bf16")
+    d = synth.device_tensors(inp, dev)
+    args = (d["q_lat"], d["q_rope"], d["kv_lat"], d["k_rope"], d["prefix_len"], d["tree_parent"],
+            d["q_len"], inp.scale)
+    for phase in ("prepare", "attend"):
+        with pytest.raises(ValueError, match="workspace"):
+            B.verify_attn(*args, max_q_len=inp.max_q_len, phase=phase)
+
+
 def test_deterministic_and_guard_bands(dev):
     inp = EDGE["ragged_batch5_h64"]("bf16")
     d = synth.device_tensors(inp, dev)

@@ -402,3 +402,40 @@ def test_brute_force_catches_planted_mistakes(kind, monkeypatch):
     out, lse = _oracle(inp)
     err = max(np.abs(out - bo).max(), np.abs(lse - bl).max())
     assert err > 1e-3, f"planted mistake {kind} went unnoticed"
+
+
+# ------------------------------------------------------------------ row-selection helper
+# verify_attn_rows is the checker used on selected rows of large batches.  It is pinned
+# against the per-row brute force (independent code) on tiny inputs, and against the
+# packed-batch oracle on selections that exercise its offsets: the last request, unsorted
+# and repeated nodes and heads, a request after one with an empty prefix.
+@pytest.mark.parametrize("seed", range(4))
+def test_rows_helper_matches_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    parents = [synth.random_tree(rng, int(rng.integers(1, 8))) for _ in range(3)]
+    prefix = [int(rng.integers(0, 12)), 0, int(rng.integers(1, 12))]
+    inp = _tiny_inputs(600 + seed, parents, prefix, heads=3)
+    bo, bl = _brute_force(inp)
+    qo = inp.q_offsets()
+    for b in range(inp.batch):
+        t = int(inp.q_len[b])
+        nodes = [int(x) for x in rng.integers(0, t, size=3)] + [t - 1, 0]
+        heads = [2, 0, 2, 1]
+        ro, rl = O.verify_attn_rows(inp, b, nodes, heads)
+        rows = qo[b] + np.asarray(nodes)
+        np.testing.assert_allclose(ro, bo[rows][:, heads], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(rl, bl[rows][:, heads], rtol=0, atol=1e-12)
+
+
+def test_rows_helper_matches_packed_oracle():
+    rng = np.random.default_rng(61)
+    parents = [synth.random_tree(rng, n) for n in (5, 33, 1, 17)]
+    inp = _tiny_inputs(62, parents, [40, 0, 7, 129], heads=8, dl=32, dr=8)
+    fo, fl = _oracle(inp)
+    qo = inp.q_offsets()
+    for b, nodes, heads in ((3, [16, 0, 4, 4], [7, 0]), (1, [32, 31, 0], [5]),
+                            (2, [0], list(range(8))), (0, [4, 2], [3, 6, 1])):
+        ro, rl = O.verify_attn_rows(inp, b, nodes, heads)
+        rows = qo[b] + np.asarray(nodes)
+        np.testing.assert_allclose(ro, fo[rows][:, heads], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(rl, fl[rows][:, heads], rtol=0, atol=1e-13)

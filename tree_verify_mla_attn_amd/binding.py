@@ -30,7 +30,7 @@ KDTREE_DTYPE_BF16 = 1
 ERRORS = {0: "OK", -1: "null pointer", -2: "bad shape", -3: "bad max_q_len", -4: "bad dtype",
           -5: "bad num_splits / workspace", -6: "non-finite scale", -7: "HIP launch failure"}
 STATUS_BITS = {1: "bad q_len", 2: "bad prefix_len", 4: "bad tree_parent", 8: "offset overflow",
-               16: "non-finite output"}
+               16: "non-finite output", 32: "bf16 input outside the fp16 range"}
 D_LATENT = 512
 D_ROPE = 64
 
@@ -349,6 +349,32 @@ def _schedule_makespan(batch: int, m_tiles: int, prefix: int, q: int, num_splits
     return worst
 
 
+def launch_uses_cut(batch: int, num_heads: int, max_q_len: int, num_splits: int,
+                    dtype: int = KDTREE_DTYPE_BF16) -> bool:
+    """Whether kdtree_verify_attn runs this launch with the last-round cut (the library's
+    rule, evaluated on the host from the same scalars): bf16 inputs, one split, every
+    XCD's queue of row tiles at most two whole rounds of its 32 CUs, and some XCD with
+    leftover row tiles that can each be cut into two or more pieces; not when
+    KDTREE_DISABLE_CUT is set."""
+    if dtype != KDTREE_DTYPE_BF16 or num_splits != 1:
+        return False
+    if os.environ.get("KDTREE_DISABLE_CUT", "0") not in ("", "0"):
+        return False
+    m_tiles = math.ceil(max_q_len * num_heads / 128)
+    full_rounds, rem = divmod(batch, 8)
+    cut = False
+    for x in range(8):
+        pos = 7 - x if full_rounds & 1 else x
+        n = (full_rounds + (1 if pos < rem else 0)) * m_tiles
+        whole = n // 32 * 32
+        left = n - whole
+        if whole > 2 * 32:
+            return False
+        if left and 32 // left >= 2:
+            cut = True
+    return cut
+
+
 def cut_applies(queues, cu_per_xcd: int = 32, max_rounds: int = 2) -> bool:
     # the library's rule for the last-round cut of a one-split bf16 launch: every XCD's
     # queue has at most max_rounds whole rounds, and some XCD has units left over that
@@ -489,17 +515,19 @@ class VerifyAttn:
         total_kv = int(kv_lat.shape[0])
         dt = KDTREE_DTYPE_BF16 if dtype == torch.bfloat16 else KDTREE_DTYPE_FP32
         need = kdtree_verify_attn_workspace_bytes(total_q, total_kv, batch, h, int(num_splits), dt)
-        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-            if phase != "all" and workspace is not None:
-                # the two halves must share the caller's buffer: a new one would hold no
-                # pre-pass output
+        if need and phase != "all":
+            # the two halves must share the caller's buffer: a fresh one would hold no
+            # pre-pass output (attend) or be thrown away (prepare)
+            if workspace is None:
+                raise ValueError(f"phase {phase!r} needs the caller's workspace "
+                                 f"({need} bytes for num_splits={num_splits})")
+            if workspace.numel() * workspace.element_size() < need:
                 raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} "
                                  f"bytes, {need} needed for num_splits={num_splits}")
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_ptr = workspace.data_ptr() if (workspace is not None and need) else 0
         ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
-        if phase == "attend" and need and workspace is None:
-            raise ValueError("phase 'attend' needs the workspace of a 'prepare' call")
         torch_stream = torch.cuda.current_stream(dev)
         args = (q_lat.data_ptr(), q_rope.data_ptr(), kv_lat.data_ptr(), k_rope.data_ptr(),
                 prefix_len.data_ptr(), tree_parent.data_ptr(), q_len.data_ptr(), float(scale),

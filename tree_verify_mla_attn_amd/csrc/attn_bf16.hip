@@ -651,16 +651,22 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
     }
     // latent part to fp16 (the scores contract it against the fp16 latent tiles); exact
     // for 2^-17 <= |x| < 65504 like the tiles themselves
+    float qmax = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const unsigned x = qf[ks][d];
-        const f16x2 hp = {(_Float16)__uint_as_float(x << 16),
-                          (_Float16)__uint_as_float(x & 0xffff0000u)};
+        const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+        qmax = fmaxf(qmax, fmaxf(fabsf(lo), fabsf(hi)));
+        const f16x2 hp = {(_Float16)lo, (_Float16)hi};
         qf[ks][d] = __builtin_bit_cast(unsigned, hp);
       }
     }
+    // a query value outside fp16's range: the bf16 path's contract is broken (the
+    // pre-pass flags latent keys the same way)
+    if (__builtin_amdgcn_ballot_w64(row_ok && !(qmax < 65504.0f)) && lane == 0 && p.status)
+      atomicOr(p.status, ST_RANGE);
     // The softmax takes a positive scale.  A negative one is moved into Q by flipping
     // every sign bit (exact: each score is then exactly negated); a zero one by zeroing
     // Q (every score is then exactly 0) with scale 1.
@@ -792,6 +798,7 @@ hipError_t launch_verify_bf16(const VerifyParams& p, hipStream_t stream) {
   const int64_t groups = (int64_t)p.batch * p.num_splits;
   if (p.cut && (p.num_splits != 1 || !p.piece_o || !p.piece_lse || !p.piece_desc))
     return hipErrorInvalidValue;
+  if (p.cut && p.piece_slots != cut_piece_slots(p.batch)) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)NUM_XCD * ((groups + NUM_XCD - 1) / NUM_XCD) * p.m_tiles +
                          (p.cut ? PIECE_SLOTS : 0);
   if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -3,6 +3,7 @@
 // launches from host scalars (device arrays are never read on the host) and enqueues
 // the kernels on the caller's stream.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -16,6 +17,13 @@ constexpr int32_t kMaxSplits = kdt::MAX_SPLITS;
 constexpr int kCutMaxRounds = 2;  // cut only when every XCD's queue has at most 2 whole rounds
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// KDTREE_DISABLE_CUT=1 in the environment switches the last-round cut off (a switch for
+// testing and timing the uncut launch; results agree up to rounding either way).
+bool cut_disabled() {
+  const char* v = getenv("KDTREE_DISABLE_CUT");
+  return v && v[0] && v[0] != '0';
+}
 
 struct WorkspaceLayout {
   size_t order_bytes, k16_bytes, part_o_bytes, part_lse_bytes, piece_bytes, total;
@@ -42,9 +50,10 @@ bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t 
   // Last-round cut pieces (bf16, one split): outputs, lse, and two int64 per unit.  They
   // share one region with the split partials (a launch uses one or the other), sized for
   // the larger, so a workspace sized for more splits also serves fewer.
+  const size_t slots = (size_t)kdt::cut_piece_slots(batch);
   w->piece_bytes = dtype == KDTREE_DTYPE_BF16
-                       ? (size_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS * (kdt::DL + 1) * sizeof(float) +
-                             (size_t)kdt::PIECE_SLOTS * 2 * sizeof(int64_t)
+                       ? slots * kdt::PIECE_ROWS * (kdt::DL + 1) * sizeof(float) +
+                             slots * 2 * sizeof(int64_t)
                        : 0;
   const size_t shared = std::max(w->part_o_bytes + w->part_lse_bytes, w->piece_bytes);
   w->total = w->order_bytes + w->k16_bytes + shared;
@@ -94,12 +103,12 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
       num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes + w.part_o_bytes) : nullptr;
   char* pw = ws + w.order_bytes + w.k16_bytes;  // the region shared with the partials
   const bool pieces = w.piece_bytes && num_splits == 1;
+  const size_t slots = (size_t)kdt::cut_piece_slots(batch);
+  p.piece_slots = pieces ? (int32_t)slots : 0;
   p.piece_o = pieces ? (float*)pw : nullptr;
-  p.piece_lse = pieces ? (float*)pw + (size_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS * kdt::DL
-                       : nullptr;
-  p.piece_desc = pieces ? (int64_t*)(pw + (size_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS *
-                                              (kdt::DL + 1) * sizeof(float))
-                        : nullptr;
+  p.piece_lse = pieces ? (float*)pw + slots * kdt::PIECE_ROWS * kdt::DL : nullptr;
+  p.piece_desc =
+      pieces ? (int64_t*)(pw + slots * kdt::PIECE_ROWS * (kdt::DL + 1) * sizeof(float)) : nullptr;
   p.status = status;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.split_ratio = split_ratio;
@@ -116,7 +125,7 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
   // rounds are few (there the leftover round is a large share of the launch); with more
   // rounds the longest-first order already fills it.
   p.cut = 0;
-  if (pieces) {
+  if (pieces && !cut_disabled()) {
     for (int x = 0; x < kdt::NUM_XCD; ++x) {
       const kdt::XcdCut c = kdt::xcd_cut(batch, p.m_tiles, x);
       if (c.whole > kCutMaxRounds * kdt::CUS_PER_XCD) { p.cut = 0; break; }
@@ -142,7 +151,7 @@ int32_t launch_attend(const kdt::VerifyParams& p, int32_t dtype, hipStream_t s) 
   }
   if (p.cut) {
     // piece lse = NaN until a piece writes it: the piece merge leaves rows no piece wrote
-    e = kdt::launch_fill_nan(p.piece_lse, (int64_t)kdt::PIECE_SLOTS * kdt::PIECE_ROWS, s);
+    e = kdt::launch_fill_nan(p.piece_lse, (int64_t)p.piece_slots * kdt::PIECE_ROWS, s);
     if (e != hipSuccess) return KDTREE_ERR_LAUNCH;
   }
   e = dtype == KDTREE_DTYPE_BF16 ? kdt::launch_verify_bf16(p, s) : kdt::launch_verify_f32(p, s);

@@ -23,7 +23,7 @@ constexpr float LN2 = 0.69314718055994530942f;
 
 // Status bits (mirrors include/kdtree_verify.h).
 constexpr int ST_BAD_QLEN = 1, ST_BAD_PREFIX = 2, ST_BAD_PARENT = 4, ST_OVERFLOW = 8,
-              ST_NONFINITE = 16;
+              ST_NONFINITE = 16, ST_RANGE = 32;
 
 struct VerifyParams {
   const void* q_lat;
@@ -48,9 +48,10 @@ struct VerifyParams {
   // Last-round cut (bf16, one split): each XCD's units after its whole rounds of
   // CUS_PER_XCD run as key pieces, written here and merged by launch_piece_merge.
   int32_t cut;         // 0: off
-  float* piece_o;      // [NUM_XCD * CUS_PER_XCD pieces, 128 rows, 512]
-  float* piece_lse;    // [NUM_XCD * CUS_PER_XCD pieces, 128 rows]
-  int64_t* piece_desc; // [NUM_XCD * CUS_PER_XCD units] x {first global row, rows}
+  int32_t piece_slots; // piece slots of the area below: CUS_PER_XCD per XCD that has work
+  float* piece_o;      // [piece_slots pieces, 128 rows, 512]
+  float* piece_lse;    // [piece_slots pieces, 128 rows]
+  int64_t* piece_desc; // [piece_slots units] x {first global row, rows}
 };
 
 // Draft-tree builder and accept.
@@ -132,6 +133,11 @@ __device__ __forceinline__ int split_begin(int P, int S, float r, int s) {
 struct XcdCut {
   int whole, left, pieces;
 };
+// XCDs that receive work from a one-split launch of `batch` requests (groups are dealt
+// to XCDs 0, 1, ... first), and so the piece slots a cut can use.
+__host__ __device__ inline int cut_piece_slots(int batch) {
+  return (batch < NUM_XCD ? batch : NUM_XCD) * CUS_PER_XCD;
+}
 __host__ __device__ inline XcdCut xcd_cut(int groups, int m_tiles, int xcd) {
   const int full_rounds = groups / NUM_XCD, rem = groups % NUM_XCD;
   const int pos = (full_rounds & 1) ? NUM_XCD - 1 - xcd : xcd;  // in the partial round

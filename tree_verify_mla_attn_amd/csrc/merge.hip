@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void piece_merge_kernel(const float* __restric
 
 hipError_t launch_piece_merge(const VerifyParams& p, hipStream_t stream) {
   if (!p.cut) return hipSuccess;
-  const int blocks = PIECE_SLOTS * PIECE_ROWS / MERGE_ROWS;
+  if (p.piece_slots <= 0 || p.piece_slots > PIECE_SLOTS) return hipErrorInvalidValue;
+  const int blocks = p.piece_slots * PIECE_ROWS / MERGE_ROWS;
   hipLaunchKernelGGL(piece_merge_kernel, dim3(blocks), dim3(256), 0, stream, p.piece_o,
                      p.piece_lse, p.piece_desc, p.out_lat, p.out_lse, p.status, p.batch,
                      p.m_tiles,

@@ -56,13 +56,13 @@ __device__ void rank_requests(const VerifyParams& p) {
 
 __global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
   __shared__ int64_t s_kvoff, s_tbase;
-  __shared__ int s_b, s_flag;
+  __shared__ int s_b, s_first_bad;
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;  // global tile index
   // Find the request owning tile g (scan over requests, 256 at a time).
   if (tid == 0) {
     s_b = -1;
-    s_flag = 0;
+    s_first_bad = p.batch;
   }
   __syncthreads();
   int64_t kv_run = 0, t_run = 0;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
       kv_len = bad ? 0 : (int64_t)pl + t;
       tiles = (kv_len + 31) / 32;
     }
-    if (bad) atomicOr(&s_flag, 1);
+    if (bad) atomicMin(&s_first_bad, b);
     // inclusive scans of kv_len and tiles across the block
     __shared__ int64_t s_scan_kv[NTHR], s_scan_t[NTHR];
     s_scan_kv[tid] = kv_len;
@@ -101,8 +101,11 @@ __global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
     __syncthreads();
   }
   if (g == 0) rank_requests(p);
-  // Malformed inputs: the attention kernel flags them; nothing sensible to convert.
-  if (s_flag || s_b < 0) return;
+  // Malformed inputs: the attention kernel flags a malformed request and skips it and
+  // every request after it (their packed offsets are unknown), but runs the requests
+  // before it; so tiles are converted exactly for the requests before the first
+  // malformed one.
+  if (s_b < 0 || s_b >= s_first_bad) return;
   const int b = s_b;
   const int64_t kvoff = s_kvoff;
   if (kvoff + p.prefix_len[b] + p.q_len[b] > p.total_kv) return;
@@ -120,6 +123,7 @@ __global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
     const int k = min(key0 + wave * 8 + e, n_keys - 1);
     w[e] = src[(kvoff + k) * 64 + lane];
   }
+  unsigned range = 0;  // bit 15 / 31: an fp16 half with an all-ones exponent (inf or NaN)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int row = wave * 8 + e;
@@ -131,9 +135,15 @@ __global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
       const f16x2 hp = {(_Float16)__uint_as_float(x[d] << 16),
                         (_Float16)__uint_as_float(x[d] & 0xffff0000u)};
       o[d] = __builtin_bit_cast(unsigned, hp);
+      range |= (o[d] & 0x7c007c00u) + 0x04000400u;
     }
     dst[row * 64 + (lane ^ ((row >> 2) & 3))] = make_uint4(o[0], o[1], o[2], o[3]);
   }
+  // A latent value outside fp16's range (|x| >= 65504: no bf16 value lies in
+  // [65504, 65536), and 65536 and up round to inf) or not finite: the contract of the bf16
+  // path is broken, and the rows that see this key are not meaningful.
+  if (__builtin_amdgcn_ballot_w64((range & 0x80008000u) != 0) && lane == 0 && p.status)
+    atomicOr(p.status, ST_RANGE);
 }
 
 }  // namespace
