@@ -72,6 +72,8 @@ extern "C" {
                                        kdtree_verify_attn_workspace_bytes */
 #define KDTREE_ERR_SCALE (-6)       /* scale not finite */
 #define KDTREE_ERR_LAUNCH (-7)      /* HIP launch failure */
+#define KDTREE_ERR_SCRATCH (-8)     /* kdtree_verify_attn_noalloc: the call needs more
+                                       scratch than KDTREE_NOALLOC_SCRATCH_BYTES */
 
 /* Device status bits OR-ed into *status (if non-NULL) by the kernels. */
 #define KDTREE_STATUS_BAD_QLEN 1u     /* some q_len[b] outside [1, max_q_len] */
@@ -196,6 +198,33 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
                                   int64_t total_q, int64_t total_kv, int32_t dtype,
                                   int32_t num_splits, float split_ratio, void* workspace,
                                   size_t workspace_bytes, int32_t* status);
+
+/*
+ * kdtree_verify_attn for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments
+ * and result as kdtree_verify_attn, without the workspace: the scratch it needs (the
+ * amount kdtree_verify_attn_workspace_bytes reports) comes from one static device array
+ * of KDTREE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until
+ * the process ends.  The call never calls hipMalloc, hipFree or any other allocating
+ * routine; on its first call on a device it looks up that device's array address.
+ *
+ *   Limit: calls whose workspace need exceeds KDTREE_NOALLOC_SCRATCH_BYTES (128 MiB)
+ *   return KDTREE_ERR_SCRATCH with nothing enqueued (for example the batch-8 workload
+ *   with 4096-key prefixes needs about 101 MB and fits; batch 64 with prefixes up to
+ *   8192 keys needs about 390 MB and does not).
+ *   Sharing: every call on one GPU uses that GPU's one array, and a call leaves its
+ *   contents behind; calls whose work overlaps on one GPU (other streams, other host
+ *   threads) race on it and must be serialised by the caller.  Nothing in the array has
+ *   to start at zero: each call writes every scratch value it later reads.
+ */
+#define KDTREE_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int32_t kdtree_verify_attn_noalloc(const void* q_lat, const void* q_rope, const void* kv_lat,
+                                   const void* k_rope, const int32_t* prefix_len,
+                                   const int32_t* tree_parent, const int32_t* q_len,
+                                   float scale, float* out_lat, float* out_lse, void* stream,
+                                   int32_t batch, int32_t num_heads, int32_t max_q_len,
+                                   int64_t total_q, int64_t total_kv, int32_t dtype,
+                                   int32_t num_splits, float split_ratio, int32_t* status);
 
 /* ------------------------------------------------------------------------------------
  * The steps on either side of verify attention in one greedy DDTree step.

@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     assert names == ["kdtree_build_ddtree", "kdtree_max_qlen", "kdtree_pack_tree",
                      "kdtree_sample_tokens", "kdtree_tree_accept",
                      "kdtree_verify_attn", "kdtree_verify_attn_attend",
-                     "kdtree_verify_attn_prepare", "kdtree_verify_attn_workspace_bytes"]
+                     "kdtree_verify_attn_noalloc", "kdtree_verify_attn_prepare",
+                     "kdtree_verify_attn_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True,
@@ -38,6 +39,8 @@ def test_library_exports_every_declared_symbol():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert re.search(r"#define KDTREE_MAX_QLEN 65\b", text)
+    assert re.search(r"#define KDTREE_NOALLOC_SCRATCH_BYTES \(128u \* 1024u \* 1024u\)", text)
+    assert B.KDTREE_NOALLOC_SCRATCH_BYTES == 128 * 1024 * 1024
     assert B.kdtree_max_qlen() == 65 == B.KDTREE_MAX_QLEN
     for code in B.ERRORS:
         if code:
@@ -283,3 +286,20 @@ def test_launch_uses_cut(monkeypatch):
     assert not B.launch_uses_cut(24, 64, 65, 1)
     monkeypatch.setenv("KDTREE_DISABLE_CUT", "1")
     assert not B.launch_uses_cut(8, 64, 65, 1)
+
+
+def test_noalloc_rejects_what_does_not_fit():
+    """A call whose workspace need exceeds the static scratch is refused before anything
+    touches the device (the need follows from host scalars alone)."""
+    kw = dict(q_lat=FAKE, q_rope=FAKE, kv_lat=FAKE, k_rope=FAKE, prefix_len=FAKE,
+              tree_parent=FAKE, q_len=FAKE, scale=0.07, out_lat=FAKE, out_lse=FAKE, stream=0,
+              batch=64, num_heads=64, max_q_len=33, total_q=2112, total_kv=306580, dtype=1,
+              num_splits=1, status=0)
+    need = B.kdtree_verify_attn_workspace_bytes(2112, 306580, 64, 64, 1, 1)
+    assert need > B.KDTREE_NOALLOC_SCRATCH_BYTES
+    assert B.kdtree_verify_attn_noalloc(**kw) == -8
+    kw.update(num_splits=16, dtype=0)
+    assert B.kdtree_verify_attn_noalloc(**kw) == -8
+    # argument errors keep their codes
+    kw.update(num_splits=1, dtype=1, total_q=66, total_kv=2000, batch=2, q_lat=0)
+    assert B.kdtree_verify_attn_noalloc(**kw) == -1

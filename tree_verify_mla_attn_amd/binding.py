@@ -28,7 +28,9 @@ KDTREE_MAX_ACCEPT_NODES = 4096
 KDTREE_DTYPE_FP32 = 0
 KDTREE_DTYPE_BF16 = 1
 ERRORS = {0: "OK", -1: "null pointer", -2: "bad shape", -3: "bad max_q_len", -4: "bad dtype",
-          -5: "bad num_splits / workspace", -6: "non-finite scale", -7: "HIP launch failure"}
+          -5: "bad num_splits / workspace", -6: "non-finite scale", -7: "HIP launch failure",
+          -8: "needs more than the static scratch"}
+KDTREE_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 STATUS_BITS = {1: "bad q_len", 2: "bad prefix_len", 4: "bad tree_parent", 8: "offset overflow",
                16: "non-finite output", 32: "bf16 input outside the fp16 range"}
 D_LATENT = 512
@@ -64,6 +66,10 @@ def load_library():
         fn.restype = i32
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                        i32, i32, i32, i64, i64, i32, i32, ctypes.c_float, vp, sz, vp]
+    lib.kdtree_verify_attn_noalloc.restype = i32
+    lib.kdtree_verify_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                               vp, i32, i32, i32, i64, i64, i32, i32,
+                                               ctypes.c_float, vp]
     lib.kdtree_build_ddtree.restype = i32
     lib.kdtree_build_ddtree.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                         vp, vp]
@@ -113,6 +119,18 @@ def kdtree_verify_attn_prepare(*args, **kw) -> int:
 def kdtree_verify_attn_attend(*args, **kw) -> int:
     """Raw call of the attention phase (same arguments as kdtree_verify_attn)."""
     return _raw("kdtree_verify_attn_attend", *args, **kw)
+
+
+def kdtree_verify_attn_noalloc(q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len,
+                               scale, out_lat, out_lse, stream, batch, num_heads, max_q_len,
+                               total_q, total_kv, dtype, num_splits, status,
+                               split_ratio=1.0) -> int:
+    """Raw call of the allocation-free variant (no workspace argument; pointers as integer
+    device addresses, split_ratio last as in _raw)."""
+    return int(load_library().kdtree_verify_attn_noalloc(
+        q_lat, q_rope, kv_lat, k_rope, prefix_len, tree_parent, q_len, ctypes.c_float(scale),
+        out_lat, out_lse, stream, batch, num_heads, max_q_len, total_q, total_kv, dtype,
+        num_splits, ctypes.c_float(split_ratio), status))
 
 
 def kdtree_build_ddtree(logp, token_ids, root_token, batch, depth, top_k, budget, q_len,

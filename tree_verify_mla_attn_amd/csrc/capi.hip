@@ -6,10 +6,19 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/kdtree_verify.h"
 
 #include "common.h"
+
+namespace kdt {
+// The allocation-free entry point's scratch: one static device array per GPU the library
+// runs on, held until the process ends.  Its name is only a host-side stand-in for the
+// symbol: host code takes the array's address on each device through hipGetSymbolAddress
+// (with that device current) and passes that pointer to the kernels, never the name.
+__device__ __align__(256) unsigned char scratch[KDTREE_NOALLOC_SCRATCH_BYTES];
+}  // namespace kdt
 
 namespace {
 
@@ -168,6 +177,24 @@ int32_t launch_attend(const kdt::VerifyParams& p, int32_t dtype, hipStream_t s) 
   return KDTREE_OK;
 }
 
+constexpr size_t kScratchBytes = (size_t)KDTREE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up once per device), or NULL on error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(kdt::scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,6 +256,36 @@ int32_t kdtree_verify_attn_attend(const void* q_lat, const void* q_rope, const v
   kdt::VerifyParams p;
   WorkspaceLayout w;
   int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
+  if (rc != KDTREE_OK) return rc;
+  return launch_attend(p, dtype, (hipStream_t)stream);
+}
+
+int32_t kdtree_verify_attn_noalloc(const void* q_lat, const void* q_rope, const void* kv_lat,
+                                   const void* k_rope, const int32_t* prefix_len,
+                                   const int32_t* tree_parent, const int32_t* q_len,
+                                   float scale, float* out_lat, float* out_lse, void* stream,
+                                   int32_t batch, int32_t num_heads, int32_t max_q_len,
+                                   int64_t total_q, int64_t total_kv, int32_t dtype,
+                                   int32_t num_splits, float split_ratio, int32_t* status) {
+  // The workspace need is known from host scalars alone: reject what does not fit before
+  // touching the device.
+  WorkspaceLayout need;
+  if (workspace_layout(total_q, total_kv, batch, num_heads, num_splits, dtype, &need) &&
+      need.total > kScratchBytes)
+    return KDTREE_ERR_SCRATCH;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  if (q_lat && q_rope && kv_lat && k_rope && prefix_len && tree_parent && q_len && out_lat &&
+      out_lse && batch >= 1 && num_heads >= 1) {
+    workspace = device_scratch();
+    if (!workspace) return KDTREE_ERR_LAUNCH;
+    workspace_bytes = kScratchBytes;
+  }
+  kdt::VerifyParams p;
+  WorkspaceLayout w;
+  int32_t rc = setup(KDTREE_SETUP_ARGS, &p, &w);
+  if (rc != KDTREE_OK) return rc;
+  rc = launch_prepare(p, w, dtype, (hipStream_t)stream);
   if (rc != KDTREE_OK) return rc;
   return launch_attend(p, dtype, (hipStream_t)stream);
 }
