@@ -8,17 +8,24 @@
 //
 // Work decomposition (one workgroup = 4 waves = 128 query rows of one request and one
 // KV split).  Rows are packed node-major, head-minor, so all heads of a node share its
-// ancestor mask and all 128 rows share every KV tile.  Each wave owns 32 rows:
-//   * Q fragment (32 rows x 576: latent part converted to fp16, rope part bf16) lives in
-//     VGPRs for the whole KV loop;
-//   * S^T = K Q^T per 32-key tile: fp16 MFMA 32x32x16 over the latent dims, bf16 over
-//     the rope dims, so each lane holds one query row and the softmax row reductions are
-//     in-register plus one lane swap;
-//   * online softmax in the log2 domain with a lazy rescale (the running max is only
-//     raised when a tile beats it by more than 2^8);
-//   * O^T += V^T P^T: fp16 MFMA 32x32x16 with P in fp16 (bf16 P is too coarse for a
-//     2e-3 relative bound); V^T operands are read from the same fp16 latent tile as K,
-//     through the transposing LDS load.
+// ancestor mask and all 128 rows share every KV tile.
+//   * Scores and softmax by rows: wave w owns rows 32w..32w+31.  Its Q fragment (32 rows x
+//     576: latent part converted to fp16, rope part bf16) lives in VGPRs for the whole
+//     KV loop; S^T = K Q^T per 32-key tile runs as fp16 MFMA 32x32x16 over the latent dims
+//     and bf16 over the rope dims, so each lane holds one query row and the softmax row
+//     reductions are in-register plus one lane swap; online softmax in the log2 domain
+//     with a lazy rescale (the running max is only raised when a tile beats it by more
+//     than 2^8).
+//   * PV by features: wave w owns features 128w..128w+127 of all 128 rows, O^T += V^T P^T
+//     as fp16 MFMA 32x32x16 with P in fp16 (bf16 P is too coarse for a 2e-3 relative
+//     bound).  Each V^T operand, read once from the fp16 latent tile through the
+//     transposing LDS load, feeds four row blocks' MFMAs; the P operands come from the
+//     softmax lanes of their owner waves through a double-buffered LDS area.
+//   * One barrier per 32-key tile.  After it, one interleaved stream of 68 MFMAs: the
+//     scores of the next tile, the PV of this tile, the copy of the tile after next, and,
+//     between the last 22 PV MFMAs, the next tile's softmax (VALU work that costs almost
+//     nothing next to independent MFMAs of the same wave, and stalls the matrix pipe when
+//     run on its own).
 // The fp16 latent tiles (converted once per call by the pre-pass) and the bf16 rope rows
 // arrive by 16-byte global->LDS DMA into a three-stage LDS ring.
 #include "common.h"
@@ -49,7 +56,9 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 //          (16 consecutive keys, one chunk each) and the transposing value reads (4
 //          consecutive keys x 4 chunks) are both bank-conflict free, and both address
 //          streams stay affine (two base registers each);
-//   K rope [32 keys][8 chunks] bf16: chunk c of key k at slot k*8 + (c ^ rswz(k)).
+//   K rope [8 chunks][32 keys] bf16, chunk-major: chunk c of key k at slot 32c + k, so
+//          a score read (32 keys x one chunk per half-wave) is 1 KB contiguous and the
+//          four rope k-steps are one affine stream (slot 64 (ks - 32) + lane).
 // Tile j serves the scores (loop trip j-1) and the values (trip j) while tile j+2 is in
 // flight: three stages.
 constexpr int K16_ROW = 68;
@@ -73,8 +82,15 @@ __shared__ __attribute__((aligned(1024))) u32x4 sKropeC[KROPE_U4];
 __shared__ int32_t sParent[MAX_QLEN];
 __shared__ int64_t sRed[3 * 4];
 __shared__ int32_t sFlag;
+// What the softmax of one trip hands to the feature-split PV of every wave, in buffers of
+// trip parity j & 1: each wave's fp16 P tile ([row block][key step][lane], 16 B each: the
+// PV B operand of that lane as the softmax left it in registers), each row's O scale for
+// the trip, and the number of the last trip in which some row's running max moved.
+__shared__ __attribute__((aligned(1024))) u32x4 sP[2][4 * 2 * 64];
+__shared__ float sAlpha[2][BM];
+__shared__ int32_t sResc[2];
+__shared__ float sInv[BM];
 
-__device__ __forceinline__ int rswz(int k) { return (k ^ (k >> 3)) & 7; }
 __device__ __forceinline__ int ksw(int k) { return (k >> 2) & 3; }
 
 template <int S> __device__ __forceinline__ u32x4* k16() {
@@ -109,19 +125,21 @@ __device__ __forceinline__ void dma_k16_row(__amdgpu_buffer_rsrc_t rsrc, int wav
                                            16, (int)lane_off, (wave * 8 + N) * 1024, 0, 0);
 }
 
-// Rope rows 8w..8w+7 of keys [key0, key0+32) (clamped to key_last), one instruction per
-// wave: lane l moves chunk (l & 7) of row 8w + (l >> 3) into its swizzled slot.
+// Rope chunks 2w, 2w+1 of keys [key0, key0+32) (clamped to key_last), one instruction per
+// wave: lane l moves chunk 2w + (l >> 5) of key l & 31 into slot 64w + l.
 template <int S>
 __device__ __forceinline__ void dma_rope(const char* k_rope_req, int key0, int key_last, int wave,
                                          int lane) {
-  const int key = wave * 8 + (lane >> 3);
-  const int k = min(key0 + key, key_last);
-  dma16(k_rope_req, (unsigned)k * (DR * 2) + (unsigned)((lane & 7) ^ rswz(key)) * 16u,
+  // recomputed from an opaque lane id on every call: kept live across the KV loop, the
+  // key index would be spilled, and its reload's vmcnt(0) would wait for this tile's copies
+  asm volatile("" : "+v"(lane));
+  const int k = min(key0 + (lane & 31), key_last);
+  dma16(k_rope_req, (unsigned)k * (DR * 2) + (unsigned)(2 * wave + (lane >> 5)) * 16u,
         krope<S>() + wave * 64);
 }
 
 // Issue the DMA of tile `tile` (keys [key0, key0+32)) into stage S.  Wave w moves fp16
-// latent rows 8w..8w+7 and rope rows 8w..8w+7.
+// latent rows 8w..8w+7 and rope chunks 2w, 2w+1.
 template <int S>
 __device__ __forceinline__ void issue_tile(const char* tile, const char* k_rope_req, int key0,
                                            int key_last, int wave, int lane) {
@@ -142,22 +160,20 @@ __device__ __forceinline__ void issue_tile(const char* tile, const char* k_rope_
 
 // Score fragment ks of the tile in stage S for this lane (key = lane & 31, half h):
 // latent k-steps 0..31 read chunk 2ks + h of the key's fp16 row, rope k-steps 32..35
-// read the bf16 rope row.
+// read chunk 2 (ks - 32) + h of its bf16 rope row.  Three affine read streams.
 struct ScoreFrags {
-  int be, bo, rrow, rkey;
+  int be, bo, rl;
   __device__ __forceinline__ ScoreFrags(int lane) {
     const int key = lane & 31, h = lane >> 5, sw = ksw(key);
     // chunk 2ks + h lands in slot 4 (ks >> 1) + ((2 (ks & 1) + h) ^ sw) of the row
     be = key * K16_ROW + (h ^ sw);
     bo = key * K16_ROW + ((2 + h) ^ sw);
-    rrow = key * 8;
-    rkey = key;
+    rl = lane;
   }
   template <int S>
   __device__ __forceinline__ u32x4 get(int ks, int h) const {
     if (ks < 32) return k16<S>()[((ks & 1) ? bo : be) + 4 * (ks >> 1)];
-    const int c = 2 * ks + h - 64;
-    return krope<S>()[rrow + (c ^ rswz(rkey))];
+    return krope<S>()[rl + 64 * (ks - 32)];
   }
 };
 
@@ -167,65 +183,6 @@ __device__ __forceinline__ f32x16 mfma_qk(int ks, const u32x4& a, const u32x4& q
                                                  __builtin_bit_cast(f16x8, q), s, 0, 0, 0);
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, q), s, 0, 0, 0);
-}
-
-// S^T (32 keys x 32 rows of this wave) for the tile in stage S.  K fragments are read
-// four MFMAs ahead of use.
-template <int S>
-__device__ __forceinline__ f32x16 qk_tile(const u32x4 (&qf)[36], int lane) {
-  const ScoreFrags fr(lane);
-  const int h = lane >> 5;
-  u32x4 a[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = fr.get<S>(i, h);
-  f32x16 s = {};
-#pragma unroll
-  for (int ks = 0; ks < 36; ++ks) {
-    if (ks + 4 < 36) a[(ks + 4) & 7] = fr.get<S>(ks + 4, h);
-    s = mfma_qk(ks, a[ks & 7], qf[ks], s);
-    __builtin_amdgcn_sched_barrier(0);  // keep each read four MFMAs ahead of its use
-  }
-  return s;
-}
-
-// Scores of the next tile (stage SQ) fused with the copy of the tile after it into stage
-// SD: nine DMAs (eight fp16 latent rows, one rope instruction), one after every four
-// score MFMAs, so the copy engine's queue drains in the shadow of the matrix pipe.
-template <int SQ, int SD>
-__device__ __forceinline__ f32x16 qk_dma(const u32x4 (&qf)[36], int lane, const char* dma_tile,
-                                         const char* k_rope_req, int k_key0, int key_last,
-                                         int wave) {
-  const ScoreFrags fr(lane);
-  const int h = lane >> 5;
-  u32x4 a[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = fr.get<SQ>(i, h);
-  f32x16 s = {};
-  int dl = lane;
-  asm volatile("" : "+v"(dl));  // per-tile lane offsets, not hoisted out of the KV loop
-  const int key0s = __builtin_amdgcn_readfirstlane(k_key0);
-  const int lasts = __builtin_amdgcn_readfirstlane(key_last);
-  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(dma_tile);
-#pragma unroll
-  for (int ks = 0; ks < 36; ++ks) {
-    if (ks + 4 < 36) a[(ks + 4) & 7] = fr.get<SQ>(ks + 4, h);
-    s = mfma_qk(ks, a[ks & 7], qf[ks], s);
-    if ((ks & 3) == 3) {
-      switch (ks >> 2) {  // 0..8, resolved at compile time in the unrolled loop
-        case 0: dma_k16_row<SD, 0>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 1: dma_k16_row<SD, 1>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 2: dma_k16_row<SD, 2>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 3: dma_k16_row<SD, 3>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 4: dma_k16_row<SD, 4>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 5: dma_k16_row<SD, 5>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 6: dma_k16_row<SD, 6>(rsrc, wave, (unsigned)dl * 16u); break;
-        case 7: dma_k16_row<SD, 7>(rsrc, wave, (unsigned)dl * 16u); break;
-        default: dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl); break;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep each read four MFMAs ahead of its use
-  }
-  return s;
 }
 
 // o[FB] += a * p (fp16 MFMA 32x32x16).  Every accumulator is an operand of every such
@@ -256,14 +213,21 @@ __device__ __forceinline__ void mfma_pv(f32x16 (&o)[16], const f16x8& a, const f
 struct ValueFrags {
   const LDS_AS char* base;
   unsigned off0, off1;
-  __device__ __forceinline__ ValueFrags(const u32x4* tile, int lane) {
+  // foff: byte offset of this wave's first feature block (4 blocks of 64 B per wave).
+  __device__ __forceinline__ ValueFrags(const u32x4* tile, int lane, int foff) {
     base = (const LDS_AS char*)(LDS_AS void*)tile;
     const int g = (lane >> 4) & 1, r = (lane >> 2) & 3, q = lane & 3, h = lane >> 5;
     // lane 4r + q of a 16-lane group reads 4 features (8 B) of key row 4h + 8j + r; the
-    // row swizzle ksw = h + 2j there, chunk 4fb + 2g + (q >> 1)
-    off0 = (unsigned)((4 * h + r) * K16_ROW * 16 + 16 * ((2 * g + (q >> 1)) ^ h) + 8 * (q & 1));
+    // row swizzle ksw = h + 2j there, chunk 4fb + 2g + (q >> 1).  The swizzle only moves
+    // chunk bits 0-1, so a feature block is a plain 64-byte offset.
+    off0 = (unsigned)((4 * h + r) * K16_ROW * 16 + 16 * ((2 * g + (q >> 1)) ^ h) + 8 * (q & 1) +
+                      foff);
     off1 = (unsigned)((4 * h + 8 + r) * K16_ROW * 16 + 16 * ((2 * g + (q >> 1)) ^ (h + 2)) +
-                      8 * (q & 1));
+                      8 * (q & 1) + foff);
+    // opaque per-lane offsets: every read stays base + offset + constant, a short address
+    // chain from the stage's LDS object, so the compiler's wait insertion keeps telling
+    // these reads apart from the copies into other stages
+    asm("" : "+v"(off0), "+v"(off1));
   }
   template <int FB, int KS>
   __device__ __forceinline__ f16x8 get() const {
@@ -274,41 +238,6 @@ struct ValueFrags {
     return f16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
   }
 };
-
-// Feature blocks FB..15 of one PV tile: the V^T operands of block FB+2 are read, then the
-// two MFMAs of block FB issue, fenced so the order holds.
-template <int FB>
-__device__ __forceinline__ void pv_block(f32x16 (&o)[16], const f16x8 (&pk)[2], f16x8 (&a)[6],
-                                         const ValueFrags& vf) {
-  if constexpr (FB < 16) {
-    if constexpr (FB + 2 < 16) {
-      a[((FB + 2) % 3) * 2] = vf.get<FB + 2, 0>();
-      a[((FB + 2) % 3) * 2 + 1] = vf.get<FB + 2, 1>();
-    }
-    mfma_pv<FB>(o, a[(FB % 3) * 2], pk[0]);
-    mfma_pv<FB>(o, a[(FB % 3) * 2 + 1], pk[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_block<FB + 1>(o, pk, a, vf);
-  }
-}
-
-// O^T += V^T P^T for the tile in stage S: 16 feature blocks x 2 key steps of fp16 MFMA
-// 32x32x16 with the 16 output accumulators pinned in AGPRs.  P passes through the s_nop
-// statement: its VALU producers (softmax) must complete before the wait states, which
-// then cover the hazard of a VALU write feeding an MFMA operand (the compiler does not
-// pad for MFMAs inside asm statements).
-template <int S>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const f16x8 (&pk)[2], int lane) {
-  const ValueFrags vf(k16<S>(), lane);
-  f16x8 a[6];
-  f16x8 pp[2] = {pk[0], pk[1]};
-  asm volatile("s_nop 4" : "+v"(pp[0]), "+v"(pp[1]));
-  a[0] = vf.get<0, 0>();
-  a[1] = vf.get<0, 1>();
-  a[2] = vf.get<1, 0>();
-  a[3] = vf.get<1, 1>();
-  pv_block<0>(o, pp, a, vf);
-}
 
 // Wait states between the last PV MFMA and VALU reads of the accumulators.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n s_nop 7\n s_nop 3"); }
@@ -366,7 +295,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 
 struct RowState {
   float m;      // running max (log2 units, scale folded in)
-  float l;      // this lane's partial sum of fp16-rounded probabilities
+  float l;      // this lane's partial sum of the probabilities (fp32, before rounding)
   float alpha;  // factor O must be scaled by before this tile's PV (1 = none)
   bool rescale; // some row of the wave needs the O rescale
 };
@@ -394,55 +323,210 @@ __device__ __forceinline__ uint32_t tile_visibility(int key0, int key_begin, int
   return vis;
 }
 
-// Online softmax of one tile: S^T (raw scores, register r <-> key 8(r/4) + 4h + r%4)
-// -> P (fp16) and the running max / sum.  `vis` = visibility bits (see above).
-// The scale c (> 0: the prologue folds a sign or a zero scale into Q) is applied inside
-// the exponent's argument, exp2(s c - m) as one fma.  The row max of the raw scores
-// times c is exactly the max of the rounded products, since rounding is monotone; masked
-// keys stay -inf.
-__device__ __forceinline__ void softmax_tile(f32x16& s, f16x8 (&pk)[2], RowState& st, float c,
-                                             bool masked, uint32_t vis, int lane) {
-  const int h = lane >> 5;
-  if (masked) {
-    const uint32_t vh = vis >> (4 * h);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
-  }
-  float mx = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = pair_max(mx) * c;
-  // Lazy rescale: the running max only moves when this tile beats it by more than
-  // 2^RESCALE_THRESHOLD; the caller then scales O by `alpha` (rare after the first tile).
-  const bool need = mx > st.m + RESCALE_THRESHOLD;  // also true when st.m == -inf
-  st.alpha = 1.0f;
-  st.rescale = __builtin_amdgcn_ballot_w64(need) != 0;
-  if (need) {
-    st.alpha = __builtin_amdgcn_exp2f(st.m - mx);
-    st.m = mx;
-    st.l *= st.alpha;
-  }
-  const float mref = st.m == -INFINITY ? 0.0f : st.m;
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    u32x4 packed;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + 2 * d], c, -mref));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + 2 * d + 1], c, -mref));
-      // round to nearest even (one v_cvt_pk_f16_f32); l sums the rounded values
-      const f16x2 hp = {(_Float16)p0, (_Float16)p1};
-      st.l = __builtin_amdgcn_fdot2(hp, ones, st.l, false);
-      packed[d] = __builtin_bit_cast(unsigned, hp);
-    }
-    pk[kk] = __builtin_bit_cast(f16x8, packed);
-  }
+// This wave's P tile of tile `jt` (two 16-byte fragments per lane), its rows' O scales
+// and, when some row's running max moved, the rescale flag, into the buffers of parity
+// jt & 1 that the feature-split PV of every wave reads after the next barrier.
+__device__ __forceinline__ void publish_p(int kk, const u32x4& packed, int wave, int lane, int jt) {
+  sP[jt & 1][(wave * 2 + kk) * 64 + lane] = packed;
+}
+__device__ __forceinline__ void publish_scale(const RowState& st, int wave, int lane, int jt) {
+  if (lane < 32) sAlpha[jt & 1][wave * 32 + lane] = st.alpha;
+  if (st.rescale && lane == 0) sResc[jt & 1] = jt;
 }
 
-// One pipelined trip of the KV loop for tile j, held in stage ST = j % 3: softmax and PV
-// of tile j, scores of tile j+1 (stage (j+1) % 3), DMA of tile j+2 into the stage tile
-// j-1 used.  One barrier per tile.
+// Online softmax of one tile: S^T (raw scores, register r <-> key 8(r/4) + 4h + r%4)
+// -> P (fp16, published to LDS) and the running max / sum.  `vis` = visibility bits (see
+// tile_visibility).  The scale c (> 0: the prologue folds a sign or a zero scale into Q)
+// is applied inside the exponent's argument, exp2(s c - m) as one fma.  The row max of the
+// raw scores times c is exactly the max of the rounded products, since rounding is
+// monotone; masked keys stay -inf.
+//
+// The work is cut into 22 steps so that it can sit between independent MFMAs: on gfx950
+// up to three or four VALU instructions per 32-cycle MFMA of the same wave cost almost
+// nothing, while the same work run on its own leaves the matrix pipe idle.
+struct SoftmaxSteps {
+  f32x16& s;
+  RowState& st;
+  const float c;
+  const bool masked;
+  const uint32_t vis;
+  const int lane, wave, jt;
+  float mx, mref, p_even;
+  u32x4 packed;
+
+  template <int K>
+  __device__ __forceinline__ void step() {
+    if constexpr (K == 0) {
+      if (masked) {
+        int ol = lane;  // the half's shift, recomputed rather than kept live in the loop
+        asm volatile("" : "+v"(ol));
+        const uint32_t vh = vis >> (4 * (ol >> 5));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
+      }
+    } else if constexpr (K == 1) {
+      mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
+    } else if constexpr (K == 2) {
+#pragma unroll
+      for (int r = 8; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    } else if constexpr (K == 3) {
+      mx = pair_max(mx) * c;
+    } else if constexpr (K == 4) {
+      // Lazy rescale: the running max only moves when this tile beats it by more than
+      // 2^RESCALE_THRESHOLD (also when st.m == -inf); O is then scaled by alpha before
+      // this tile's PV (rare after the first tile).
+      const bool need = mx > st.m + RESCALE_THRESHOLD;
+      st.alpha = 1.0f;
+      st.rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+      if (need) {
+        st.alpha = __builtin_amdgcn_exp2f(st.m - mx);
+        st.m = mx;
+        st.l *= st.alpha;
+      }
+      mref = st.m == -INFINITY ? 0.0f : st.m;
+    } else if constexpr (K == 5) {
+      publish_scale(st, wave, lane, jt);
+    } else if constexpr (K >= 6 && K < 22) {
+      constexpr int E = K - 6;  // score register E: p = exp2(s c - m)
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[E], c, -mref));
+      // l sums the fp32 values with plain adds (a v_dot2 next to the MFMAs would stall
+      // the matrix pipe ~20 cycles each); P for the MFMA is rounded to nearest even
+      st.l += pe;
+      if constexpr (E % 2 == 0) {
+        p_even = pe;
+      } else {
+        const f16x2 hp = {(_Float16)p_even, (_Float16)pe};
+        packed[(E % 8) / 2] = __builtin_bit_cast(unsigned, hp);
+        if constexpr (E % 8 == 7) publish_p(E / 8, packed, wave, lane, jt);
+      }
+    }
+  }
+};
+
+// The MFMA stream of one trip, after its barrier: the scores of tile j+1 (stage SQ), the
+// PV of tile j (stage SV), the copy of tile j+2 into stage SD, and the softmax of tile
+// j+1.  PV is split by features: this wave owns feature blocks 4w..4w+3 (128 features) of
+// all 128 rows, accumulator 4 fbl + rb = local feature block fbl of row block rb.  Its B
+// operands (P) come from the LDS copies every wave's softmax wrote before the barrier; each
+// V^T operand, read once, feeds the four row blocks' MFMAs.
+//
+// 68 MFMA slots.  Slots 0..45: the 36 score MFMAs with PV MFMAs 0..9 in between (six
+// scores, then one PV per three scores), so that tile j+1's scores are complete at slot
+// 45; slots 46..67: PV MFMAs 10..31, each followed by one step of tile j+1's softmax.  PV
+// MFMAs run in the order (key step, feature block, row block).  K fragments are read three
+// score MFMAs ahead, V^T fragments three PV MFMAs ahead, the P fragments of key step 1
+// four ahead (each replaces the key-step-0 fragment of its row block after that one's
+// last use).  The nine copies go in the first part, so that they have most of a trip to
+// land before the next barrier waits for them.
+template <int SQ, int SD, int SV>
+struct TripStream {
+  static constexpr int KA = 3;  // K fragments read this many score MFMAs ahead
+  f32x16& s;
+  f32x16 (&o)[16];
+  const u32x4 (&qf)[36];
+  const ScoreFrags fr;
+  const ValueFrags vf;
+  const __amdgpu_buffer_rsrc_t rsrc;
+  const char* k_rope_req;
+  const int key0s, lasts, wave, lane, dl, j, par;
+  SoftmaxSteps& sm;
+  int resc;
+  u32x4 ka[4];
+  f16x8 va[2];
+  f16x8 pf[4];
+
+  __device__ __forceinline__ TripStream(f32x16& s_, f32x16 (&o_)[16], const u32x4 (&qf_)[36],
+                                        int lane_, int wave_, const char* dma_tile,
+                                        const char* k_rope_req_, int k_key0, int key_last,
+                                        int j_, SoftmaxSteps& sm_)
+      : s(s_), o(o_), qf(qf_), fr(lane_), vf(k16<SV>(), lane_, wave_ * 256),
+        rsrc(tile_rsrc(dma_tile)), k_rope_req(k_rope_req_),
+        key0s(__builtin_amdgcn_readfirstlane(k_key0)),
+        lasts(__builtin_amdgcn_readfirstlane(key_last)), wave(wave_), lane(lane_),
+        dl(lane_), j(j_), par(j_ & 1), sm(sm_), resc(-1) {}
+
+  // P fragment (key step ks, row block rb): lane `lane` of the owner wave's softmax.
+  __device__ __forceinline__ f16x8 pfrag(int ks, int rb) const {
+    return __builtin_bit_cast(f16x8, sP[par][(rb * 2 + ks) * 64 + lane]);
+  }
+
+  __device__ __forceinline__ void run() {
+    const int h = lane >> 5;
+    // LDS reads return in order: the first score MFMA's operand goes first
+#pragma unroll
+    for (int i = 0; i < KA; ++i) ka[i] = fr.get<SQ>(i, h);
+    va[0] = vf.get<0, 0>();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) pf[rb] = pfrag(0, rb);
+    resc = sResc[par];
+    __builtin_amdgcn_sched_barrier(0);
+    slot<0>();
+  }
+
+  // O *= alpha for every row whose running max moved with tile j (rare after the first
+  // tiles).  Trip 0 needs none: O is still zero.
+  __device__ __forceinline__ void rescale() {
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(resc) == j, 0) && j > 0) {
+      mfma_drain();
+      int ol = lane;  // recomputed address: nothing of this rare path stays live
+      asm volatile("" : "+v"(ol));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const float a = sAlpha[par][rb * 32 + (ol & 31)];
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) o[4 * fb + rb] = scale_acc(o[4 * fb + rb], a);
+      }
+      // wait states between the VALU writes of the accumulators and the MFMAs reading them
+      asm volatile("s_nop 4");
+    }
+  }
+
+  template <int T>
+  __device__ __forceinline__ void slot() {
+    if constexpr (T < 68) {
+      constexpr int G = (T - 6) / 4, R = (T - 6) % 4;
+      constexpr int QK = T < 6 ? T : (T < 46 ? (R != 0 ? 6 + 3 * G + R - 1 : -1) : -1);
+      constexpr int PV = T < 6 ? -1 : (T < 46 ? (R == 0 ? G : -1) : 10 + (T - 46));
+      if constexpr (PV == 0) {
+        rescale();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (QK >= 0 && QK + KA < 36) ka[(QK + KA) & 3] = fr.get<SQ>(QK + KA, lane >> 5);
+      if constexpr (PV >= 0 && PV % 4 == 1 && PV / 4 + 1 < 8) {
+        constexpr int V = PV / 4 + 1;  // next V^T fragment (key step V / 4, block V % 4)
+        va[V & 1] = vf.get<V % 4, V / 4>();
+      }
+      if constexpr (T % 5 == 1 && T <= 41) {
+        constexpr int N = T / 5;  // copies 0..8
+        if constexpr (N < 8)
+          dma_k16_row<SD, N>(rsrc, wave, (unsigned)dl * 16u);
+        else
+          dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl);
+      }
+      // the score chain starts from zero: s held tile j's scores, consumed last trip
+      if constexpr (QK >= 0) s = mfma_qk(QK, ka[QK & 3], qf[QK], QK == 0 ? f32x16{} : s);
+      if constexpr (PV >= 0) {
+        constexpr int V = PV / 4;
+        mfma_pv<(V % 4) * 4 + PV % 4>(o, va[V & 1], pf[PV % 4]);
+        // the last key-step-0 use of this row block's P: fetch its key-step-1 fragment
+        if constexpr (PV >= 12 && PV < 16) pf[PV % 4] = pfrag(1, PV % 4);
+      }
+      if constexpr (T >= 46) sm.step<T - 46>();
+      __builtin_amdgcn_sched_barrier(0);
+      slot<T + 1>();
+    }
+  }
+};
+
+// One trip of the KV loop for tile j, held in stage ST = j % 3.  On entry every wave has
+// published tile j's P (the previous trip, or the prologue for tile 0).  The trip's one
+// barrier then makes those visible and vouches for tile j+1's copy and for every wave
+// being done with tile j-1's stage; the stream then runs the scores of tile j+1, the PV of
+// tile j, the copy of tile j+2 into the stage tile j-1 used, and tile j+1's softmax,
+// which publishes its P for the next trip.
 struct TileLoop {
   const char* k_rope;
   const char* k16;  // this split's first fp16 latent tile
@@ -453,33 +537,34 @@ struct TileLoop {
   float c;
   int tid, wave, lane;
 
+  __device__ __forceinline__ bool tile_masked(int key0) const {
+    return key0 < k_first || key0 + BN > mask_from;
+  }
+
   template <int ST>
   __device__ __forceinline__ void iteration(int j, f32x16& s_cur, f32x16 (&o)[16], RowState& st,
                                             const u32x4 (&qf)[36]) const {
-    const int key0 = k_begin + j * BN;
-    const bool masked = key0 < k_first || key0 + BN > mask_from;
-    const uint32_t vis = masked ? tile_visibility(key0, k_first, k_end, prefix, node, anc)
-                                : 0xffffffffu;
-    f16x8 pk[2];
-    softmax_tile(s_cur, pk, st, c, masked, vis, lane);
-    if (__builtin_expect(st.rescale, 0)) {
-      mfma_drain();
-#pragma unroll
-      for (int fb = 0; fb < 16; ++fb) o[fb] = scale_acc(o[fb], st.alpha);
-    }
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      // Past the last tile the copy repeats the last one: a harmless refill of a stage
-      // nobody reads any more.
-      const int jd = min(j + 2, n_tiles - 1);
-      s_cur = qk_dma<(ST + 1) % 3, (ST + 2) % 3>(qf, lane, k16 + (int64_t)jd * TILE_BYTES, k_rope,
-                                                 key0 + 2 * BN, key_last, wave);
-    }
-    pv_tile<ST>(o, pk, lane);
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Tile j+1's softmax.  On the last trip the stream's scores are of a stale stage: every
+    // key is masked, which leaves the running max and sum as they are (and publishes a P
+    // nobody reads).
+    const int key1 = k_begin + (j + 1) * BN;
+    const bool last = j + 1 >= n_tiles;
+    const bool masked = last || tile_masked(key1);
+    const uint32_t vis = last ? 0u
+                       : (masked ? tile_visibility(key1, k_first, k_end, prefix, node, anc)
+                                 : 0xffffffffu);
+    SoftmaxSteps sm{s_cur, st, c, masked, vis, lane, wave, j + 1};
+    // One stream for every trip (a second PV call site would cost the accumulators their
+    // fixed AGPRs).  On the last trip its copy repeats the last tile into the stage tile
+    // j-1 used: a harmless refill of a stage nobody reads any more (waited for before the
+    // epilogue reuses the ring).
+    const int jd = min(j + 2, n_tiles - 1);
+    TripStream<(ST + 1) % 3, (ST + 2) % 3, ST> ts(s_cur, o, qf, lane, wave,
+                                                  k16 + (int64_t)jd * TILE_BYTES, k_rope,
+                                                  k_begin + (j + 2) * BN, key_last, j, sm);
+    ts.run();
   }
 };
 
@@ -694,68 +779,77 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   for (int fb = 0; fb < 16; ++fb) o[fb] = f32x16{};
   RowState st{-INFINITY, 0.0f, 1.0f, false};
 
-  // Pipeline: trip j runs the softmax and PV of tile j (stage j % 3) while the scores of
-  // tile j+1 are computed; the DMA of tile j+2 is in flight.  One barrier per tile.
+  // Pipeline: trip j runs the softmax of tile j (stage j % 3), then the scores of tile
+  // j+1 interleaved with the PV of tile j, while the DMA of tile j+2 is in flight.  One
+  // barrier per tile (trip 0's waits for tile 1).
   if (tbase + (P + T + BN - 1) / BN > p.k16_tiles) {  // cannot happen for valid offsets
     if (tid == 0 && p.status) atomicOr(p.status, ST_OVERFLOW);
     return;
   }
   const char* k16_split = (const char*)p.k16 + (tbase + k_begin / BN) * TILE_BYTES;
   issue_tile<0>(k16_split, k_rope, k_begin, key_last, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (n_tiles > 1) issue_tile<1>(k16_split + TILE_BYTES, k_rope, k_begin + BN, key_last, wave, lane);
-  f32x16 s_cur = qk_tile<0>(qf, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Trip -1 runs the same stream as every other trip: tile 0's scores and softmax, the copy
+  // of tile 1, and a PV of zero P over a zeroed stage 2 (a no-op on O).  So tile 0 needs
+  // no code of its own: a second copy of the softmax or of the PV would cost the output
+  // accumulators their fixed AGPRs.
+  for (int i = tid; i < K16_U4; i += NTHR) sK16c[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < 4 * 2 * 64; i += NTHR) sP[1][i] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < 2) sResc[tid] = -1;
 
   TileLoop tl{k_rope, k16_split, k_begin, k_first, k_end, key_last, n_tiles, mask_from,
               P, node, anc, c, tid, wave, lane};
-  for (int j = 0; j < n_tiles; j += 3) {
-    tl.iteration<0>(j, s_cur, o, st, qf);
+  f32x16 s_cur = {};
+  // Trip j works on tile j in stage (j + 3) % 3.
+  for (int j = -1; j < n_tiles; j += 3) {
+    tl.iteration<2>(j, s_cur, o, st, qf);
     if (j + 1 >= n_tiles) break;
-    tl.iteration<1>(j + 1, s_cur, o, st, qf);
+    tl.iteration<0>(j + 1, s_cur, o, st, qf);
     if (j + 2 >= n_tiles) break;
-    tl.iteration<2>(j + 2, s_cur, o, st, qf);
+    tl.iteration<1>(j + 2, s_cur, o, st, qf);
   }
   mfma_drain();
 
   // ---- finalize -------------------------------------------------------------------
+  // The softmax lanes of a row (its owner wave) hold l and m; every wave holds 128
+  // features of all 128 rows of O.  1 / l goes to the other waves through LDS.
   const float l_tot = pair_sum(st.l);
   // A cut piece may hold only tree-tail keys that a row cannot see: its partial is then
   // (0, -inf), as for an empty split.  (A whole split always holds the node itself.)
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_tot > 0.0f ? st.m * LN2 + logf(l_tot) : -INFINITY;
-  // A wave's 32 rows are consecutive global rows, so its output block is contiguous.
-  const int wrow0 = m0 + wave * 32;
-  const int wrows = min(32, rows - wrow0);  // rows of this wave that exist (may be <= 0)
-  const int64_t gbase = qoff * H + wrow0;
-  float* const out = piece >= 0 ? p.piece_o + ((int64_t)pslot * BM + wave * 32) * DL
-                   : S == 1    ? p.out_lat + gbase * DL
-                               : p.part_o + ((int64_t)split * p.total_q * H + gbase) * DL;
+  if (lane < 32) sInv[wave * 32 + lane] = inv;
+  // The tile ring is free once every wave has finished the last tile and the last trip's
+  // refill has landed.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int trows = min(BM, rows - m0);  // rows of this row tile that exist
+  // The workgroup's rows are consecutive global rows; this wave writes features
+  // [128 w, 128 w + 128) of each.
+  float* const out = (piece >= 0 ? p.piece_o + (int64_t)pslot * BM * DL
+                      : S == 1  ? p.out_lat + (qoff * H + m0) * DL
+                                : p.part_o + ((int64_t)split * p.total_q * H + qoff * H + m0) * DL) +
+                     wave * 128;
   // The accumulator layout gives each lane 16-byte pieces of one row, so direct stores
-  // would touch 32 rows per instruction.  Instead each wave passes its block through LDS
-  // (the tile ring, free once every wave has finished the last tile), 128 features at a
-  // time, and every store instruction then writes 512 contiguous bytes of two rows.
-  // No wave has a tile read or copy outstanding here (the last trip waited for its reads
-  // before its MFMAs, and issued no copy), so a bare barrier suffices.
-  asm volatile("s_barrier" ::: "memory");
-  if (wrows <= 0) return;
+  // would touch 32 rows per instruction.  Instead each wave passes its block through LDS,
+  // one row block (32 rows x 128 features) at a time, and every store instruction then
+  // writes 512 contiguous bytes of two rows.
   LDS_AS char* stage = (LDS_AS char*)(LDS_AS void*)((wave < 2) ? sK16a : sK16b) + (wave & 1) * EPI_WAVE_BYTES;
   const int r = lane & 31;
 #pragma unroll
-  for (int chunk = 0; chunk < 4; ++chunk) {
-    // keep each chunk's accumulator reads inside the chunk: read all at once, the 256
+  for (int rb = 0; rb < 4; ++rb) {
+    if (rb * 32 >= trows) continue;
+    // keep each row block's accumulator reads inside it: read all at once, the 256
     // values would not fit the VGPRs next to the accumulators
     __builtin_amdgcn_sched_barrier(0);
+    const float ir = sInv[rb * 32 + r];
 #pragma unroll
-    for (int f4 = 0; f4 < 4; ++f4) {
-      const f32x16 t = read_acc_here(o[chunk * 4 + f4]);
+    for (int fb = 0; fb < 4; ++fb) {
+      const f32x16 t = read_acc_here(o[4 * fb + rb]);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = {t[4 * q4] * inv, t[4 * q4 + 1] * inv, t[4 * q4 + 2] * inv,
-                         t[4 * q4 + 3] * inv};
-        *(LDS_AS f32x4*)(stage + r * EPI_ROW_BYTES + (f4 * 32 + q4 * 8 + h * 4) * 4) = v;
+        const f32x4 v = {t[4 * q4] * ir, t[4 * q4 + 1] * ir, t[4 * q4 + 2] * ir,
+                         t[4 * q4 + 3] * ir};
+        *(LDS_AS f32x4*)(stage + r * EPI_ROW_BYTES + (fb * 32 + q4 * 8 + h * 4) * 4) = v;
       }
     }
     wave_sync();
@@ -763,19 +857,17 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       v[i] = *(const LDS_AS f32x4*)(stage + (2 * i + h) * EPI_ROW_BYTES + r * 16);
-    float* dst = out + (int64_t)h * DL + chunk * 128 + r * 4;
-    if (wrows == 32) {
+    float* dst = out + (int64_t)(rb * 32 + h) * DL + r * 4;
+    if (rb * 32 + 32 <= trows) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (2 * i + h < wrows) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
+        if (rb * 32 + 2 * i + h < trows) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
     }
     wave_sync();
   }
-  // last, so that no global store is outstanding when the first LDS write above waits
-  // for the tile copies
   if (row_ok && h == 0) {
     if (piece >= 0)
       p.piece_lse[(int64_t)pslot * BM + (row - m0)] = lse;
