@@ -21,8 +21,10 @@ Draw (T > 0), per row r and vocabulary entry i, all in float32 except the genera
           low 32 bits for even i, high 32 bits for odd i
   u     = (2 * (x32 >> 9) + 1) * 2^-24, in (0, 1)
   c     = log2(e) / T                                    (float32 constants, rounded)
-  z     = logit * c - log2(-log2(u))                     (each operation rounded)
+  z     = logit * c - L(-L(u))                           (each operation rounded)
   token = argmax_i z, lowest i on ties; -1 if every logit is -inf.
+L is the float32 base-2 logarithm of ``log2_f32`` below, a fixed sequence of rounded
+float32 operations, so that a GPU evaluating the same sequence draws the same tokens.
 z is log2(e) times the Gumbel-max key logit / T - ln(-ln u), less the constant
 log2(ln 2): the same argmax, so token ~ softmax(logit / T) (the Gumbel-max identity), with
 base-2 logarithms throughout.  T = 0: token = argmax_i logit.
@@ -71,6 +73,39 @@ def philox4x64_10(ctr, key):
     return c0, c1, c2, c3
 
 
+# log2(1 + f) = (2 / ln 2) atanh(s), s = f / (2 + f): the classical series
+# ln z = 2 (s + s^3 / 3 + s^5 / 5 + ...) with s = (z - 1) / (z + 1), z = 1 + f, times log2(e).
+# Coefficient k of the series in s^2 (float32): 2 / ((2k + 1) ln 2).
+LOG2_SERIES = [np.float32(2.0 / ((2 * k + 1) * np.log(2.0))) for k in range(5)]
+_SQRT2_BITS = np.uint32(0x3FB504F3)  # float32 sqrt(2), rounded
+
+
+def log2_f32(x) -> np.ndarray:
+    """Base-2 logarithm of positive normal float32 values as a fixed sequence of float32
+    operations, each rounded to nearest (no fused multiply-add):
+      x = 2^e m, m in [1, 2) from the bits; if m > sqrt(2): m = m / 2, e = e + 1 (exact);
+      f = m - 1 (exact), s = f / (2 + f), z = s * s;
+      p = ((((A4 z + A3) z + A2) z + A1) z + A0), A_k = 2 / ((2k + 1) ln 2);
+      L = e + s * p.
+    |s| <= 0.172, so the series' truncation after s^9 is below 2e-9 relative; the
+    rounding keeps L within a few ulp of log2(x), and exact at powers of two."""
+    xf = np.asarray(x, np.float32)
+    bits = xf.view(np.uint32)
+    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int32) - np.int32(127)
+    mbits = (bits & np.uint32(0x7FFFFF)) | np.uint32(0x3F800000)
+    big = mbits > _SQRT2_BITS
+    mbits = np.where(big, mbits - np.uint32(0x00800000), mbits).astype(np.uint32)
+    e = np.where(big, e + 1, e)
+    m = mbits.view(np.float32)
+    f = (m - np.float32(1.0)).astype(np.float32)
+    s = (f / (np.float32(2.0) + f).astype(np.float32)).astype(np.float32)
+    z = (s * s).astype(np.float32)
+    p = LOG2_SERIES[4]
+    for a in (LOG2_SERIES[3], LOG2_SERIES[2], LOG2_SERIES[1], LOG2_SERIES[0]):
+        p = ((p * z).astype(np.float32) + a).astype(np.float32)
+    return (e.astype(np.float32) + (s * p).astype(np.float32)).astype(np.float32)
+
+
 def uniforms(rows, vocab: int, seed: int, offset: int) -> np.ndarray:
     """u in (0, 1) (float32) for vocabulary entries 0..vocab-1 of the given row index(es):
     shape [vocab] for one row, [len(rows), vocab] for several."""
@@ -96,9 +131,9 @@ def perturbed(logits: np.ndarray, temperature: float, rows, seed: int, offset: i
     lg = np.asarray(logits, np.float32)
     c = np.float32(LOG2E) / np.float32(temperature)
     u = uniforms(rows, lg.shape[-1], seed, offset)
-    g = np.log2(-np.log2(u))
+    g = log2_f32(-log2_f32(u))
     with np.errstate(invalid="ignore"):
-        return (lg * c).astype(np.float32) - g.astype(np.float32)
+        return (lg * c).astype(np.float32) - g
 
 
 def sample_tokens(logits: np.ndarray, temperature: float, seed: int, offset: int,

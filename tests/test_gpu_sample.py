@@ -1,12 +1,11 @@
 """GPU parity of the temperature draw (kdtree_sample_tokens) against the CPU oracle
 (oracle/sample_f32.py), and of the temperature accept (draw, then the greedy walk).
 
-Bar: T = 0 is exact (an argmax with the lowest index on ties).  T > 0: the drawn token
-equals the oracle's; the only admissible difference is a near-tie of the perturbed values
-z, where both sides' logarithms (correct to about an ulp, not bit-identical) can order
-the top two differently.  Such a row must have |z_gpu - z_oracle| <= 1e-5 (1 + |z|) in
-the oracle's own values, and at most one row per case may use it.  A frequency test on
-the GPU alone checks the draw against softmax(logits / T).
+Bar: every drawn token equals the oracle's, at T = 0 (an argmax with the lowest index on
+ties) and at T > 0: both sides evaluate the keys with the same float32 operations, the
+base-2 logarithm included (a fixed sequence of rounded operations), so the perturbed values
+and their argmax agree bit for bit.  A frequency test on the GPU alone checks the draw
+against softmax(logits / T).
 """
 import numpy as np
 import pytest
@@ -51,14 +50,7 @@ def compare(name, logits, temperature, seed, offset, got):
     want = S.sample_tokens(logits, temperature, seed, offset)
     bad = np.nonzero(got != want)[0]
     print(f"[{name}] T={temperature} rows={len(got)} differing={len(bad)}", flush=True)
-    if temperature == 0:
-        np.testing.assert_array_equal(got, want)
-        return
-    assert len(bad) <= 1, (name, bad)
-    for r in bad:
-        z = S.perturbed(logits[r], temperature, int(r), seed, offset).astype(np.float64)
-        assert got[r] >= 0 and abs(z[got[r]] - z[want[r]]) <= 1e-5 * (1 + abs(z[want[r]])), \
-            (name, int(r), int(got[r]), int(want[r]))
+    np.testing.assert_array_equal(got, want, err_msg=f"{name}: rows {bad[:8]}")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

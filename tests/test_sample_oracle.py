@@ -107,8 +107,11 @@ def _mutant(old, new):
 
 @pytest.mark.parametrize("old,new", [
     ("(lg * c)", "(lg * np.float32(temperature))"),               # T applied the wrong way
-    ("g = np.log2(-np.log2(u))", "g = -np.log2(-np.log2(u))"),   # Gumbel sign flipped
-    ("g = np.log2(-np.log2(u))", "g = np.log2(u)"),              # not a Gumbel variate
+    ("g = log2_f32(-log2_f32(u))", "g = -log2_f32(-log2_f32(u))"),   # Gumbel sign flipped
+    ("g = log2_f32(-log2_f32(u))", "g = log2_f32(u)"),               # not a Gumbel variate
+    ("LOG2_SERIES = [np.float32(2.0 / ((2 * k + 1) * np.log(2.0))) for k in range(5)]",
+     "LOG2_SERIES = [np.float32(2.0 / ((2 * k + 1) * np.log(10.0))) for k in range(5)]"),
+    # a logarithm of the wrong base: keys scaled, so softmax(logit / T) no longer holds
     ("np.float32(LOG2E) / np.float32(temperature)",
      "np.float32(1.0) / np.float32(temperature)"),               # base mismatch
 ])
@@ -131,3 +134,53 @@ def test_planted_generator_mistake_fails_the_numpy_pin():
     raw = g.random_raw(4)
     mine = mod.philox4x64_10(tuple(np.array([v], np.uint64) for v in (8, 8, 9, 10)), (123, 456))
     assert [int(w[0]) for w in mine] != [int(x) for x in raw]
+
+
+# ------------------------------------------------------------------ the float32 logarithm
+def test_log2_f32_accuracy_and_exact_points():
+    """The draw's float32 base-2 logarithm (a fixed sequence of rounded float32 operations,
+    which the GPU evaluates the same way) against float64 log2: within 3 ulp of the result
+    over 30 binades of random values and all powers of two, within 3e-7 relative on (0.5, 1)
+    where -log2(u) near 0 decides the argmax, exact at powers of two."""
+    rng = np.random.default_rng(900)
+    x = np.concatenate([(2.0 ** rng.uniform(-126, 127, 400000)).astype(np.float32),
+                        rng.uniform(0.5, 1.0, 200000).astype(np.float32),
+                        (1.0 - np.arange(1, 30000) * 2.0 ** -24).astype(np.float32),
+                        (1.0 + np.arange(1, 30000) * 2.0 ** -23).astype(np.float32)])
+    got = S.log2_f32(x).astype(np.float64)
+    ref = np.log2(x.astype(np.float64))
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    nz = ref != 0
+    assert (np.abs(got - ref)[nz] <= 3 * ulp[nz]).all()
+    near = (x > 0.5) & (x < 1)
+    assert (np.abs(got - ref)[near] <= 3e-7 * np.abs(ref[near])).all()
+    k = np.arange(-126, 128)
+    assert np.array_equal(S.log2_f32(np.float32(2.0) ** k.astype(np.float32)), k.astype(np.float32))
+    assert S.log2_f32(np.float32(1.0)) == 0.0
+
+
+def test_log2_f32_is_a_fixed_float32_sequence():
+    """The steps are float32 operations in a fixed order: recomputing them one by one with
+    Python floats rounded to float32 after every operation gives the same bits."""
+    import struct
+
+    def f32(v):
+        return struct.unpack("f", struct.pack("f", v))[0]
+    a = [float(c) for c in S.LOG2_SERIES]
+    rng = np.random.default_rng(901)
+    for x in (2.0 ** rng.uniform(-30, 30, 300)).astype(np.float32):
+        bits = int(np.array(x).view(np.uint32))
+        e = ((bits >> 23) & 0xFF) - 127
+        mb = (bits & 0x7FFFFF) | 0x3F800000
+        if mb > 0x3FB504F3:
+            mb -= 0x800000
+            e += 1
+        m = struct.unpack("f", struct.pack("I", mb))[0]
+        f = f32(m - 1.0)
+        s = f32(f / f32(2.0 + f))
+        z = f32(s * s)
+        p = a[4]
+        for c in (a[3], a[2], a[1], a[0]):
+            p = f32(f32(p * z) + c)
+        want = f32(float(e) + f32(s * p))
+        assert float(S.log2_f32(x)) == want, float(x)

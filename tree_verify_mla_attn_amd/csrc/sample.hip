@@ -10,8 +10,10 @@
 // "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) with counter (i / 8, r, 0, 0)
 // and key (seed, offset): word (i / 2) % 4 of the block, its low 32 bits for even i and
 // high 32 bits for odd i, x32 -> (2 (x32 >> 9) + 1) 2^-24.  Then, rounding each step in
-// float32, z_i = logit_i * (log2(e) / T) - log2(-log2(u_i)), and the token is the argmax
-// of z, lowest index on ties.  z is log2(e) times the Gumbel-max key logit / T - ln(-ln u)
+// float32, z_i = logit_i * (log2(e) / T) - L(-L(u_i)), with L the float32 base-2
+// logarithm log2_seq below (a fixed sequence of rounded operations, so the draws are
+// reproducible bit for bit on the host), and the token is the argmax of z, lowest index
+// on ties.  z is log2(e) times the Gumbel-max key logit / T - ln(-ln u)
 // less a constant, so token ~ softmax(logit / T).  T = 0: argmax of the logits.  A row
 // whose logits are all -inf yields -1.
 //
@@ -147,12 +149,41 @@ __device__ __forceinline__ float uniform_of(unsigned x32) {
   return __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, x32, 9)) - 0x1.fffffep-1f;
 }
 
-// log2(-log2(u)) with the hardware base-2 log: within an ulp relative to the exact value
-// over all u here, also near 1, where the small -log2(u) decide the argmax (u >= 2^-24
-// and -log2(u) >= 2^-24 / ln 2 are normal numbers).  It falls as u rises.
-__device__ __forceinline__ float gumbel_log2(float u) {
-  return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+// Base-2 logarithm of a positive normal float as a fixed sequence of float32 operations,
+// each rounded to nearest, none fused, so that any other evaluation of the same sequence
+// (the host's) gets the same bits:
+//   x = 2^e m, m in [1, 2) from the bits; if m > sqrt(2): m = m / 2, e = e + 1 (exact);
+//   f = m - 1 (exact), s = f / (2 + f) (correctly rounded division), z = s s;
+//   p = (((A4 z + A3) z + A2) z + A1) z + A0, with A_k = 2 / ((2k + 1) ln 2) in float32;
+//   log2 x = e + s p.
+// This is the classical series ln z = 2 (s + s^3/3 + s^5/5 + ...), s = (z-1)/(z+1), in
+// base 2.  |s| <= 0.172 keeps the truncation after s^9 below 2e-9 relative; the result is
+// within a few ulp of log2 x (relative near x = 1, where f is exact), and exact at powers
+// of two.
+__device__ __forceinline__ float log2_seq(float x) {
+#pragma clang fp contract(off)
+  constexpr float A0 = 0x1.715476p+1f, A1 = 0x1.ec709ep-1f, A2 = 0x1.2776c6p-1f,
+                  A3 = 0x1.a61762p-2f, A4 = 0x1.484b14p-2f;
+  const unsigned bits = __float_as_uint(x);
+  int e = (int)((bits >> 23) & 0xffu) - 127;
+  unsigned mb = (bits & 0x7fffffu) | 0x3f800000u;
+  if (mb > 0x3fb504f3u) {  // m > sqrt(2) (float32 sqrt(2) rounds down)
+    mb -= 0x00800000u;
+    e += 1;
+  }
+  const float f = __uint_as_float(mb) - 1.0f;
+  const float s = f / (2.0f + f);  // correctly rounded: HIP's default float division
+  const float z = s * s;
+  float p = A4 * z + A3;
+  p = p * z + A2;
+  p = p * z + A1;
+  p = p * z + A0;
+  return (float)e + s * p;
 }
+
+// log2(-log2(u)) for u in [2^-24, 1 - 2^-24]: both arguments are normal numbers.  It falls
+// as u rises, up to the few-ulp rounding of the two logarithms.
+__device__ __forceinline__ float gumbel_log2(float u) { return log2_seq(-log2_seq(u)); }
 
 // u <= 1 - 2^-24 gives -log2(-log2 u) <= 23.47, so no key exceeds its scaled logit by more
 // than this (plus a relative margin for the rounding of large scaled logits).
@@ -224,8 +255,8 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
     for (int k = 0; k < 8; ++k) w[k] = (unsigned)(c[k >> 1] >> (32 * (k & 1)));
     // Second test, with the block's own uniforms: u rises with its word and a key falls
     // with gumbel_log2(u), so no key of the block exceeds sm - gumbel_log2(u of the
-    // largest word).  The margin covers the logarithms' error (about an ulp each, at most
-    // ~2e-7 absolute through the outer one) and the rounding of the products.
+    // largest word).  The margin covers the logarithms' rounding (a few ulp each, at most
+    // ~6e-7 absolute through the outer one) and the rounding of the products.
     const unsigned wmax = max(max(max(w[0], w[1]), max(w[2], w[3])),
                               max(max(w[4], w[5]), max(w[6], w[7])));
     const float gmin = gumbel_log2(uniform_of(wmax));
