@@ -413,14 +413,50 @@ struct SoftmaxSteps {
 // operands (P) come from the LDS copies every wave's softmax wrote before the barrier; each
 // V^T operand, read once, feeds the four row blocks' MFMAs.
 //
-// 68 MFMA slots.  Slots 0..45: the 36 score MFMAs with PV MFMAs 0..9 in between (six
-// scores, then one PV per three scores), so that tile j+1's scores are complete at slot
-// 45; slots 46..67: PV MFMAs 10..31, each followed by one step of tile j+1's softmax.  PV
-// MFMAs run in the order (key step, feature block, row block).  K fragments are read three
-// score MFMAs ahead, V^T fragments three PV MFMAs ahead, the P fragments of key step 1
-// four ahead (each replaces the key-step-0 fragment of its row block after that one's
-// last use).  The nine copies go in the first part, so that they have most of a trip to
-// land before the next barrier waits for them.
+// 68 MFMA slots in two parts.  Part A (36 + PA slots): the 36 score MFMAs, the first Q0
+// alone, then with PV MFMAs 0..PA-1 spread evenly between them, so that tile j+1's scores
+// are complete at its end.  Part B: PV MFMAs PA..31, with the 22 steps of tile j+1's
+// softmax spread evenly over them.  PV MFMAs run in the order (key step, feature block,
+// row block).  K fragments are read three score MFMAs ahead, V^T fragments three PV MFMAs
+// ahead, the P fragments of key step 1 four ahead (each replaces the key-step-0 fragment
+// of its row block after that one's last use).  The nine copies are spread over the
+// first DMA_SPAN slots, so that they have most of a trip to land before the next barrier
+// waits for them.
+#ifndef KDT_SCHED_Q0
+#define KDT_SCHED_Q0 6
+#endif
+#ifndef KDT_SCHED_PA
+#define KDT_SCHED_PA 10
+#endif
+#ifndef KDT_SCHED_DMA_SPAN
+#define KDT_SCHED_DMA_SPAN 45
+#endif
+struct Sched {
+  static constexpr int Q0 = KDT_SCHED_Q0, PA = KDT_SCHED_PA, LA = 36 + PA, NB = 32 - PA;
+  static constexpr int DMA_SPAN = KDT_SCHED_DMA_SPAN;
+  static_assert(Q0 >= 1 && Q0 <= 36 && PA >= 1 && PA <= 31, "schedule shape");
+  // part A, slot t >= Q0: PV MFMAs placed by an even (Bresenham) spread
+  static constexpr int pv_done(int t) { return t < Q0 ? 0 : ((t - Q0 + 1) * PA) / (LA - Q0); }
+  static constexpr int qk(int T) {
+    return T < Q0 ? T
+         : (T < LA ? (pv_done(T) > pv_done(T - 1) ? -1 : T - pv_done(T)) : -1);
+  }
+  static constexpr int pv(int T) {
+    return T < Q0 ? -1 : (T < LA ? (pv_done(T) > pv_done(T - 1) ? pv_done(T) - 1 : -1)
+                                 : PA + (T - LA));
+  }
+  // softmax steps [sm_begin, sm_end) run in part-B slot T
+  static constexpr int sm_begin(int T) { return T < LA ? 0 : ((T - LA) * 22) / NB; }
+  static constexpr int sm_end(int T) { return T < LA ? 0 : ((T - LA + 1) * 22) / NB; }
+  // copy N (0..8) goes in slot dma_slot(N)
+  static constexpr int dma_slot(int N) { return 1 + (N * (DMA_SPAN - 1)) / 8; }
+  static constexpr int dma_at(int T) {
+    for (int n = 0; n < 9; ++n)
+      if (dma_slot(n) == T) return n;
+    return -1;
+  }
+};
+
 template <int SQ, int SD, int SV>
 struct TripStream {
   static constexpr int KA = 3;  // K fragments read this many score MFMAs ahead
@@ -484,12 +520,19 @@ struct TripStream {
     }
   }
 
+  template <int K, int KE>
+  __device__ __forceinline__ void sm_steps() {
+    if constexpr (K < KE) {
+      sm.step<K>();
+      sm_steps<K + 1, KE>();
+    }
+  }
+
   template <int T>
   __device__ __forceinline__ void slot() {
     if constexpr (T < 68) {
-      constexpr int G = (T - 6) / 4, R = (T - 6) % 4;
-      constexpr int QK = T < 6 ? T : (T < 46 ? (R != 0 ? 6 + 3 * G + R - 1 : -1) : -1);
-      constexpr int PV = T < 6 ? -1 : (T < 46 ? (R == 0 ? G : -1) : 10 + (T - 46));
+      constexpr int QK = Sched::qk(T);
+      constexpr int PV = Sched::pv(T);
       if constexpr (PV == 0) {
         rescale();
         __builtin_amdgcn_sched_barrier(0);
@@ -499,8 +542,8 @@ struct TripStream {
         constexpr int V = PV / 4 + 1;  // next V^T fragment (key step V / 4, block V % 4)
         va[V & 1] = vf.get<V % 4, V / 4>();
       }
-      if constexpr (T % 5 == 1 && T <= 41) {
-        constexpr int N = T / 5;  // copies 0..8
+      if constexpr (Sched::dma_at(T) >= 0) {
+        constexpr int N = Sched::dma_at(T);  // copies 0..8
         if constexpr (N < 8)
           dma_k16_row<SD, N>(rsrc, wave, (unsigned)dl * 16u);
         else
@@ -514,7 +557,7 @@ struct TripStream {
         // the last key-step-0 use of this row block's P: fetch its key-step-1 fragment
         if constexpr (PV >= 12 && PV < 16) pf[PV % 4] = pfrag(1, PV % 4);
       }
-      if constexpr (T >= 46) sm.step<T - 46>();
+      sm_steps<Sched::sm_begin(T), Sched::sm_end(T)>();
       __builtin_amdgcn_sched_barrier(0);
       slot<T + 1>();
     }
