@@ -97,9 +97,10 @@ int32_t kdtree_max_qlen(void);
 
 /* Workspace bytes kdtree_verify_attn needs (0 = none).  Returns 0 for invalid sizes.
  * Regions (each rounded up to 256 bytes):
- *   bf16 inputs: the request schedule (batch int32) and fp16 copies of the latent rows,
- *     key-major in 32-key tiles, both written by a pre-pass of the same call:
- *     batch * 4 and (total_kv / 32 + batch + 1) * 32 KB bytes;
+ *   bf16 inputs: the request schedule (one 64-byte record per request: its index in
+ *     longest-first order, packed offsets and status) and fp16 copies of the latent
+ *     rows, key-major in 32-key tiles, both written by a pre-pass of the same call:
+ *     batch * 64 and (total_kv / 32 + batch + 1) * 32 KB bytes;
  *   one region of the larger of
  *     num_splits > 1: split partial outputs num_splits * total_q * num_heads * 512 * 4
  *       bytes, then their log-sum-exps num_splits * total_q * num_heads * 4 bytes;
@@ -175,7 +176,8 @@ int32_t kdtree_verify_attn(const void* q_lat, const void* q_rope, const void* kv
  *       prefix_len and q_len only; the other pointers must still be valid values.
  *   kdtree_verify_attn_attend    enqueues the attention (and, with num_splits > 1,
  *       the merge), reading the workspace that a prepare call with the same
- *       kv_lat, prefix_len, q_len, batch, max_q_len, total_kv and dtype filled.  Until
+ *       kv_lat, prefix_len, q_len, batch, max_q_len, total_q, total_kv and dtype
+ *       filled.  Until
  *       any of those inputs change, one prepare may serve several attend calls.
  *
  * kdtree_verify_attn(args) == kdtree_verify_attn_prepare(args) followed by

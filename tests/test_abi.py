@@ -52,27 +52,27 @@ def test_workspace_bytes():
         return -(-x // 256) * 256
     # fp32, one split: nothing
     assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 0) == 0
-    # bf16, one split: the request order, the fp16 latent tiles, and the area of the
+    # bf16, one split: the request records (64 bytes each), the fp16 latent tiles, and the area of the
     # last-round cut: 32 piece slots per XCD that receives work (min(batch, 8) XCDs),
     # each 128 rows x (512 + 1) fp32, then 2 int64 per slot
     def pieces(batch):
         slots = 32 * min(batch, 8)
         return slots * 128 * 513 * 4 + slots * 16
-    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 1) == up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768) + pieces(2)
-    assert B.kdtree_verify_attn_workspace_bytes(9, 300, 1, 64, 1, 1) == up(4) + up((300 // 32 + 1 + 1) * 32768) + pieces(1)
-    assert B.kdtree_verify_attn_workspace_bytes(900, 9000, 30, 8, 1, 1) == up(30 * 4) + up((9000 // 32 + 30 + 1) * 32768) + pieces(30)
+    assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 1, 1) == up(2 * 64) + up((5000 // 32 + 2 + 1) * 32768) + pieces(2)
+    assert B.kdtree_verify_attn_workspace_bytes(9, 300, 1, 64, 1, 1) == up(64) + up((300 // 32 + 1 + 1) * 32768) + pieces(1)
+    assert B.kdtree_verify_attn_workspace_bytes(900, 9000, 30, 8, 1, 1) == up(30 * 64) + up((9000 // 32 + 30 + 1) * 32768) + pieces(30)
     # bf16, 16 splits: tiles + partial outputs + partial lse (larger than the cut area,
     # which shares their region)
     tq, tkv, b, h, s = 260, 131332, 4, 64, 16
     rows = tq * h
-    want = up(b * 4) + up((tkv // 32 + b + 1) * 32768) + up(s * rows * 512 * 4) + up(s * rows * 4)
+    want = up(b * 64) + up((tkv // 32 + b + 1) * 32768) + up(s * rows * 512 * 4) + up(s * rows * 4)
     assert B.kdtree_verify_attn_workspace_bytes(tq, tkv, b, h, s, 1) == want
     # bf16, 2 splits of a small batch: the partials (26 MB) outgrow the cut area (17 MB)
     assert B.kdtree_verify_attn_workspace_bytes(100, 5000, 2, 64, 2, 1) == \
-        up(2 * 4) + up((5000 // 32 + 2 + 1) * 32768) + up(2 * 6400 * 512 * 4) + up(2 * 6400 * 4)
+        up(2 * 64) + up((5000 // 32 + 2 + 1) * 32768) + up(2 * 6400 * 512 * 4) + up(2 * 6400 * 4)
     # ... and with few rows the cut area is the larger
     assert B.kdtree_verify_attn_workspace_bytes(10, 500, 2, 8, 2, 1) == \
-        up(2 * 4) + up((500 // 32 + 2 + 1) * 32768) + pieces(2)
+        up(2 * 64) + up((500 // 32 + 2 + 1) * 32768) + pieces(2)
     # never smaller for more splits
     for dt in (0, 1):
         sizes = [B.kdtree_verify_attn_workspace_bytes(165, 1500, 5, 64, k, dt) for k in range(1, 40)]

@@ -80,7 +80,6 @@ __shared__ __attribute__((aligned(1024))) u32x4 sKropeA[KROPE_U4];
 __shared__ __attribute__((aligned(1024))) u32x4 sKropeB[KROPE_U4];
 __shared__ __attribute__((aligned(1024))) u32x4 sKropeC[KROPE_U4];
 __shared__ int32_t sParent[MAX_QLEN];
-__shared__ int64_t sRed[3 * 4];
 __shared__ int32_t sFlag;
 // What the softmax of one trip hands to the feature-split PV of every wave, in buffers of
 // trip parity j & 1: each wave's fp16 P tile ([row block][key step][lane], 16 B each: the
@@ -470,7 +469,7 @@ struct TripStream {
   const int key0s, lasts, wave, lane, dl, j, par;
   SoftmaxSteps& sm;
   int resc;
-  u32x4 ka[4];
+  u32x4 ka[KA + 1];
   f16x8 va[2];
   f16x8 pf[4];
 
@@ -537,7 +536,7 @@ struct TripStream {
         rescale();
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (QK >= 0 && QK + KA < 36) ka[(QK + KA) & 3] = fr.get<SQ>(QK + KA, lane >> 5);
+      if constexpr (QK >= 0 && QK + KA < 36) ka[(QK + KA) % (KA + 1)] = fr.get<SQ>(QK + KA, lane >> 5);
       if constexpr (PV >= 0 && PV % 4 == 1 && PV / 4 + 1 < 8) {
         constexpr int V = PV / 4 + 1;  // next V^T fragment (key step V / 4, block V % 4)
         va[V & 1] = vf.get<V % 4, V / 4>();
@@ -550,7 +549,7 @@ struct TripStream {
           dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl);
       }
       // the score chain starts from zero: s held tile j's scores, consumed last trip
-      if constexpr (QK >= 0) s = mfma_qk(QK, ka[QK & 3], qf[QK], QK == 0 ? f32x16{} : s);
+      if constexpr (QK >= 0) s = mfma_qk(QK, ka[QK % (KA + 1)], qf[QK], QK == 0 ? f32x16{} : s);
       if constexpr (PV >= 0) {
         constexpr int V = PV / 4;
         mfma_pv<(V % 4) * 4 + PV % 4>(o, va[V & 1], pf[PV % 4]);
@@ -611,6 +610,77 @@ struct TileLoop {
   }
 };
 
+// LDS writes of this workgroup before its later LDS reads: LDS traffic only, so copies
+// into LDS and global loads in flight stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The latent part of one wave's 32 query rows, moved through LDS.  Loaded directly in the
+// fragment layout, each 16-byte load would take 32 bytes from each of 32 rows; here each
+// 16-byte global->LDS copy instruction moves 512 contiguous bytes of two rows (whole
+// cache lines), in two halves of the 1 KB rows (half PS = bytes [512 PS, 512 PS + 512)).
+// Area of wave w: the latent buffer of stage 1 (waves 0, 1) or stage 2 (waves 2, 3), at
+// (w & 1) * 16640 bytes.  Copy i puts row i's half at 1040 i and row i + 16's at
+// 1040 i + 512; the 16-byte pad between copies keeps the fragment reads (16 rows of one
+// chunk per 16 lanes) free of bank conflicts.  Rows past the row tile's end repeat its
+// last row.
+struct QStage {
+  static constexpr int COPY_BYTES = 1040;
+  static_assert(2 * 16 * COPY_BYTES <= K16_U4 * 16, "two waves' areas per latent buffer");
+  const char* wave_row0;  // the wave's first row (clamped to the last row)
+  int rel_last;           // the last row, relative to wave_row0
+  int lane;
+  u32x4* area;
+
+  __device__ __forceinline__ QStage(const void* q_lat, int64_t req_row0, int wave_row, int rows,
+                                    int wave, int lane_)
+      : lane(lane_) {
+    const int first = min(wave_row, rows - 1);
+    wave_row0 = (const char*)q_lat + (req_row0 + first) * (DL * 2);
+    rel_last = rows - 1 - first;
+    area = ((wave < 2) ? sK16b : sK16c) + (wave & 1) * (16 * COPY_BYTES / 16);
+  }
+  template <int PS>
+  __device__ __forceinline__ void issue() const {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = min(i + 16 * (lane >> 5), rel_last);
+      dma16(wave_row0, (unsigned)(r * (DL * 2) + PS * 512 + (lane & 31) * 16),
+            area + i * (COPY_BYTES / 16));
+    }
+  }
+  // fragments 16 PS .. 16 PS + 15: lane (row r = lane & 31, half h) takes chunk 2 ks + h
+  template <int PS>
+  __device__ __forceinline__ void read(u32x4 (&qf)[36]) const {
+    const int r = lane & 31, h = lane >> 5;
+    const LDS_AS char* base = (const LDS_AS char*)(LDS_AS void*)area + (r & 15) * COPY_BYTES +
+                              (r >> 4) * 512 + h * 16;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qf[16 * PS + k] = *(const LDS_AS u32x4*)(base + k * 32);
+  }
+};
+
+// Latent fragments K0 .. K0 + 15 (bf16) to fp16, tracking the largest magnitude.  The
+// scores contract them against the fp16 latent tiles; exact for 2^-17 <= |x| < 65504
+// like the tiles themselves.  One fragment at a time: left to itself the scheduler widens
+// all values to fp32 first and runs out of registers.
+template <int K0>
+__device__ __forceinline__ void q_to_fp16(u32x4 (&qf)[36], float& qmax) {
+#pragma unroll
+  for (int ks = K0; ks < K0 + 16; ++ks) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const unsigned x = qf[ks][d];
+      const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+      qmax = fmaxf(qmax, fmaxf(fabsf(lo), fabsf(hi)));
+      const f16x2 hp = {(_Float16)lo, (_Float16)hi};
+      qf[ks][d] = __builtin_bit_cast(unsigned, hp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -653,82 +723,28 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const bool geo = p.split_ratio < 1.0f;
   const int rank = geo ? grank % p.batch : grank / p.num_splits;
   const int split = geo ? grank / p.batch : grank % p.num_splits;
-  int b = p.order ? p.order[rank] : rank;
-  if (b < 0 || b >= p.batch) b = rank;
-  b = __builtin_amdgcn_readfirstlane(b);
-
-  // ---- packed offsets: exclusive prefix sums over earlier requests ---------------
-  int64_t qoff = 0, kvoff = 0, tbase = 0;
-  int bad = 0;
-  for (int i = tid; i < b; i += NTHR) {
-    const int t = p.q_len[i], pl = p.prefix_len[i];
-    bad |= (t < 1 || t > p.max_q_len) ? ST_BAD_QLEN : 0;
-    bad |= pl < 0 ? ST_BAD_PREFIX : 0;
-    qoff += t;
-    kvoff += (int64_t)pl + t;
-    tbase += ((int64_t)pl + t + TILE_KEYS - 1) / TILE_KEYS;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    qoff += __shfl_xor(qoff, off);
-    kvoff += __shfl_xor(kvoff, off);
-    tbase += __shfl_xor(tbase, off);
-    bad |= __shfl_xor(bad, off);
-  }
-  if (tid == 0) sFlag = 0;
-  __syncthreads();
-  if (lane == 0) {
-    sRed[wave] = qoff;
-    sRed[4 + wave] = kvoff;
-    sRed[8 + wave] = tbase;
-    if (bad) atomicOr(&sFlag, bad);
-  }
-  __syncthreads();
-  qoff = uniform64(sRed[0] + sRed[1] + sRed[2] + sRed[3]);
-  kvoff = uniform64(sRed[4] + sRed[5] + sRed[6] + sRed[7]);
-  tbase = uniform64(sRed[8] + sRed[9] + sRed[10] + sRed[11]);
-  const int T = p.q_len[b];
-  const int P = p.prefix_len[b];
-  int flag = __builtin_amdgcn_readfirstlane(sFlag);
-  if (T < 1 || T > p.max_q_len) flag |= ST_BAD_QLEN;
-  if (P < 0) flag |= ST_BAD_PREFIX;
-  if (!flag && (qoff + T > p.total_q || kvoff + P + T > p.total_kv || P > MAX_REQUEST_KEYS - T))
-    flag |= ST_OVERFLOW;
+  // ---- this request: lengths, packed offsets and status, from its record ----------
+  const ReqRec* const rec = p.req + rank;
+  const int flag = __builtin_amdgcn_readfirstlane(rec->flag);
   if (flag) {
     if (tid == 0 && p.status) atomicOr(p.status, flag);
     return;
   }
+  const int T = __builtin_amdgcn_readfirstlane(rec->q_len);
+  const int P = __builtin_amdgcn_readfirstlane(rec->prefix_len);
+  const int64_t qoff = uniform64(rec->qoff);
+  const int64_t kvoff = uniform64(rec->kvoff);
+  const int64_t tbase = uniform64(rec->tbase);
   const int H = p.num_heads;
   const int rows = T * H;
   const int m0 = mt * BM;
   if (m0 >= rows) return;
 
-  // ---- parents -> LDS, validated -------------------------------------------------
-  __syncthreads();
-  if (tid == 0) sFlag = 0;
-  __syncthreads();
-  if (tid < T) {
-    const int pa = p.tree_parent[qoff + tid];
-    const bool ok = tid == 0 ? pa == -1 : (pa >= 0 && pa < tid);
-    sParent[tid] = ok ? pa : -1;
-    if (!ok) atomicOr(&sFlag, ST_BAD_PARENT);
-  }
-  __syncthreads();
-  const int pflag = __builtin_amdgcn_readfirstlane(sFlag);
-  if (pflag) {
-    if (tid == 0 && p.status) atomicOr(p.status, pflag);
-    return;
-  }
-
-  // ---- this lane's query row, node and ancestor-or-self mask ----------------------
+  // ---- this lane's query row and node ----------------------------------------------
   const int row = m0 + wave * 32 + (lane & 31);
   const bool row_ok = row < rows;
   const int crow = row_ok ? row : rows - 1;
   const int node = crow / H;
-  uint64_t anc = 0;
-  for (int x = node, hops = 0; x >= 0 && hops <= MAX_QLEN; ++hops) {
-    if (x < 64) anc |= 1ull << x;
-    x = sParent[x];
-  }
 
   // ---- key range of this split (or piece) --------------------------------------------
   const int S = p.num_splits;
@@ -767,45 +783,6 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
     return;
   }
 
-  // ---- Q fragment -> VGPRs (B operand of S^T = K Q^T) ----------------------------
-  u32x4 qf[36];
-  {
-    const char* ql = (const char*)p.q_lat + grow * (DL * 2);
-    const char* qr = (const char*)p.q_rope + grow * (DR * 2);
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-      const int c = 2 * ks + h;
-      qf[ks] = ks < 32 ? *(const u32x4*)(ql + c * 16) : *(const u32x4*)(qr + (c - 64) * 16);
-    }
-    // latent part to fp16 (the scores contract it against the fp16 latent tiles); exact
-    // for 2^-17 <= |x| < 65504 like the tiles themselves
-    float qmax = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const unsigned x = qf[ks][d];
-        const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
-        qmax = fmaxf(qmax, fmaxf(fabsf(lo), fabsf(hi)));
-        const f16x2 hp = {(_Float16)lo, (_Float16)hi};
-        qf[ks][d] = __builtin_bit_cast(unsigned, hp);
-      }
-    }
-    // a query value outside fp16's range: the bf16 path's contract is broken (the
-    // pre-pass flags latent keys the same way)
-    if (__builtin_amdgcn_ballot_w64(row_ok && !(qmax < 65504.0f)) && lane == 0 && p.status)
-      atomicOr(p.status, ST_RANGE);
-    // The softmax takes a positive scale.  A negative one is moved into Q by flipping
-    // every sign bit (exact: each score is then exactly negated); a zero one by zeroing
-    // Q (every score is then exactly 0) with scale 1.
-    const unsigned flip = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
-    const unsigned keep = p.scale_log2 == 0.0f ? 0u : 0xffffffffu;
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) qf[ks][d] = (qf[ks][d] & keep) ^ flip;
-  }
-
   const char* k_rope = (const char*)p.k_rope + kvoff * (DR * 2);  // this request's rows
   // Tiles are 32-aligned in the request's key stream (the fp16 latent tiles are); a split
   // whose range starts mid-tile (only the last split, when the prefix is short) masks the
@@ -817,6 +794,73 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const int mask_from = min(P, k_end);  // tiles ending at or before this key are unmasked
   const float c = p.scale_log2 > 0.0f ? p.scale_log2 : (p.scale_log2 < 0.0f ? -p.scale_log2 : 1.0f);
 
+  // ---- the prologue's memory traffic, all in flight together ----------------------
+  // the rope part of Q straight into the fragments, the request's parents, tile 0 into
+  // stage 0 and the first half of the latent part of this wave's Q rows into its staging
+  // area.
+  u32x4 qf[36];
+  {
+    const char* qr = (const char*)p.q_rope + grow * (DR * 2);
+#pragma unroll
+    for (int ks = 32; ks < 36; ++ks) qf[ks] = *(const u32x4*)(qr + (2 * ks + h - 64) * 16);
+  }
+  const int pa = tid < T ? p.tree_parent[qoff + tid] : -1;
+  const char* k16_split = (const char*)p.k16 + (tbase + k_begin / BN) * TILE_BYTES;
+  issue_tile<0>(k16_split, k_rope, k_begin, key_last, wave, lane);
+  const QStage qs(p.q_lat, qoff * H, m0 + wave * 32, rows, wave, lane);
+  qs.issue<0>();
+
+  // ---- parents -> LDS, validated -------------------------------------------------
+  if (tid == 0) sFlag = 0;
+  lds_barrier();
+  if (tid < T) {
+    const bool ok = tid == 0 ? pa == -1 : (pa >= 0 && pa < tid);
+    sParent[tid] = ok ? pa : -1;
+    if (!ok) atomicOr(&sFlag, ST_BAD_PARENT);
+  }
+  lds_barrier();
+  const int pflag = __builtin_amdgcn_readfirstlane(sFlag);
+  if (pflag) {
+    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS may land after the workgroup ends
+    if (tid == 0 && p.status) atomicOr(p.status, pflag);
+    return;
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T) ----------------------------------------
+  // Read the first half of the latent Q, reload the area with the second half, and
+  // convert the first half while that copy is in flight.  (Explicit waits: the copies
+  // write LDS behind the compiler's back.)
+  __builtin_amdgcn_s_waitcnt(0);
+  qs.read<0>(qf);
+  __builtin_amdgcn_s_waitcnt(0);  // LDS reads done before the area is refilled
+  qs.issue<1>();
+  float qmax = 0.0f;
+  q_to_fp16<0>(qf, qmax);
+  // this lane's node's ancestor-or-self mask, also while the copy is in flight
+  uint64_t anc = 0;
+  for (int x = node, hops = 0; x >= 0 && hops <= MAX_QLEN; ++hops) {
+    if (x < 64) anc |= 1ull << x;
+    x = sParent[x];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  qs.read<1>(qf);
+  q_to_fp16<16>(qf, qmax);
+  // a query value outside fp16's range: the bf16 path's contract is broken (the
+  // pre-pass flags latent keys the same way)
+  if (__builtin_amdgcn_ballot_w64(row_ok && !(qmax < 65504.0f)) && lane == 0 && p.status)
+    atomicOr(p.status, ST_RANGE);
+  // The softmax takes a positive scale.  A negative one is moved into Q by flipping
+  // every sign bit (exact: each score is then exactly negated); a zero one by zeroing
+  // Q (every score is then exactly 0) with scale 1.
+  {
+    const unsigned flip = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
+    const unsigned keep = p.scale_log2 == 0.0f ? 0u : 0xffffffffu;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) qf[ks][d] = (qf[ks][d] & keep) ^ flip;
+  }
+
   f32x16 o[16];
 #pragma unroll
   for (int fb = 0; fb < 16; ++fb) o[fb] = f32x16{};
@@ -825,16 +869,12 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   // Pipeline: trip j runs the softmax of tile j (stage j % 3), then the scores of tile
   // j+1 interleaved with the PV of tile j, while the DMA of tile j+2 is in flight.  One
   // barrier per tile (trip 0's waits for tile 1).
-  if (tbase + (P + T + BN - 1) / BN > p.k16_tiles) {  // cannot happen for valid offsets
-    if (tid == 0 && p.status) atomicOr(p.status, ST_OVERFLOW);
-    return;
-  }
-  const char* k16_split = (const char*)p.k16 + (tbase + k_begin / BN) * TILE_BYTES;
-  issue_tile<0>(k16_split, k_rope, k_begin, key_last, wave, lane);
   // Trip -1 runs the same stream as every other trip: tile 0's scores and softmax, the copy
   // of tile 1, and a PV of zero P over a zeroed stage 2 (a no-op on O).  So tile 0 needs
   // no code of its own: a second copy of the softmax or of the PV would cost the output
-  // accumulators their fixed AGPRs.
+  // accumulators their fixed AGPRs.  Stage 2 held Q staging areas: every wave is done
+  // with them after this barrier.
+  __syncthreads();
   for (int i = tid; i < K16_U4; i += NTHR) sK16c[i] = u32x4{0u, 0u, 0u, 0u};
   for (int i = tid; i < 4 * 2 * 64; i += NTHR) sP[1][i] = u32x4{0u, 0u, 0u, 0u};
   if (tid < 2) sResc[tid] = -1;

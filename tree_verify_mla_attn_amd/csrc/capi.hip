@@ -35,11 +35,11 @@ bool cut_disabled() {
 }
 
 struct WorkspaceLayout {
-  size_t order_bytes, k16_bytes, part_o_bytes, part_lse_bytes, piece_bytes, total;
+  size_t req_bytes, k16_bytes, part_o_bytes, part_lse_bytes, piece_bytes, total;
   int64_t k16_tiles;
 };
 
-// Workspace: [request order + fp16 latent tiles (bf16 inputs)] [split partial outputs +
+// Workspace: [request records + fp16 latent tiles (bf16 inputs)] [split partial outputs +
 // split lse, or (bf16, one split) the last-round cut pieces], each region 256-byte
 // aligned.  Latent tiles: one 32 KB tile per 32 keys
 // of every request, bounded by total_kv / 32 + batch (each request adds at most one
@@ -51,7 +51,7 @@ bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t 
     return false;
   if (total_q > ((int64_t)1 << 40) || total_kv > ((int64_t)1 << 40)) return false;
   w->k16_tiles = dtype == KDTREE_DTYPE_BF16 ? total_kv / kdt::TILE_KEYS + batch + 1 : 0;
-  w->order_bytes = dtype == KDTREE_DTYPE_BF16 ? round_up((size_t)batch * 4, 256) : 0;
+  w->req_bytes = dtype == KDTREE_DTYPE_BF16 ? round_up((size_t)batch * sizeof(kdt::ReqRec), 256) : 0;
   w->k16_bytes = round_up((size_t)w->k16_tiles * (size_t)kdt::TILE_BYTES, 256);
   const size_t rows = (size_t)total_q * (size_t)num_heads;
   w->part_o_bytes = num_splits > 1 ? round_up((size_t)num_splits * rows * kdt::DL * sizeof(float), 256) : 0;
@@ -65,7 +65,7 @@ bool workspace_layout(int64_t total_q, int64_t total_kv, int32_t batch, int32_t 
                              slots * 2 * sizeof(int64_t)
                        : 0;
   const size_t shared = std::max(w->part_o_bytes + w->part_lse_bytes, w->piece_bytes);
-  w->total = w->order_bytes + w->k16_bytes + shared;
+  w->total = w->req_bytes + w->k16_bytes + shared;
   return true;
 }
 
@@ -104,13 +104,13 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
   p.out_lat = out_lat;
   p.out_lse = out_lse;
   char* ws = (char*)workspace;
-  p.order = w.order_bytes ? (int32_t*)ws : nullptr;
-  p.k16 = w.k16_bytes ? ws + w.order_bytes : nullptr;
+  p.req = w.req_bytes ? (kdt::ReqRec*)ws : nullptr;
+  p.k16 = w.k16_bytes ? ws + w.req_bytes : nullptr;
   p.k16_tiles = w.k16_tiles;
-  p.part_o = num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes) : nullptr;
+  p.part_o = num_splits > 1 ? (float*)(ws + w.req_bytes + w.k16_bytes) : nullptr;
   p.part_lse =
-      num_splits > 1 ? (float*)(ws + w.order_bytes + w.k16_bytes + w.part_o_bytes) : nullptr;
-  char* pw = ws + w.order_bytes + w.k16_bytes;  // the region shared with the partials
+      num_splits > 1 ? (float*)(ws + w.req_bytes + w.k16_bytes + w.part_o_bytes) : nullptr;
+  char* pw = ws + w.req_bytes + w.k16_bytes;  // the region shared with the partials
   const bool pieces = w.piece_bytes && num_splits == 1;
   const size_t slots = (size_t)kdt::cut_piece_slots(batch);
   p.piece_slots = pieces ? (int32_t)slots : 0;

@@ -25,6 +25,22 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr int ST_BAD_QLEN = 1, ST_BAD_PREFIX = 2, ST_BAD_PARENT = 4, ST_OVERFLOW = 8,
               ST_NONFINITE = 16, ST_RANGE = 32;
 
+// One request as the bf16 attention kernel needs it, written by the pre-pass at the
+// request's rank (longest KV first): one record per workgroup prologue instead of a
+// prefix sum over the earlier requests.  `flag` holds the status bits the kernel reports
+// for the request: a malformed request and every request after it in index order (whose
+// packed offsets are then unknown) are flagged, and 0 means the offsets are in range.
+struct ReqRec {
+  int32_t b;           // request index
+  int32_t q_len, prefix_len;
+  int32_t flag;
+  int64_t qoff;        // sum of q_len over earlier requests
+  int64_t kvoff;       // sum of prefix_len + q_len over earlier requests
+  int64_t tbase;       // first fp16 latent tile of the request
+  int64_t pad[3];
+};
+static_assert(sizeof(ReqRec) == 64, "one record per 64 bytes");
+
 struct VerifyParams {
   const void* q_lat;
   const void* q_rope;
@@ -39,7 +55,7 @@ struct VerifyParams {
   float* part_lse;   // [num_splits, total_q*H]
   int32_t* status;   // nullable
   void* k16;         // bf16 path: fp16 latent tiles (32 keys each) written by the pre-pass
-  int32_t* order;    // bf16 path: requests by descending KV length (written by the pre-pass)
+  ReqRec* req;       // bf16 path: [batch] by rank, longest KV first (written by the pre-pass)
   float scale_log2;  // scale * log2(e)
   float split_ratio; // 1: equal splits; < 1: geometric splits, largest first
   int32_t batch, num_heads, max_q_len, num_splits, m_tiles;

@@ -12,8 +12,9 @@
 // keeps the conversion out of the attention loop, where each tile is consumed by every
 // row tile of its request.
 //
-// Workgroup 0 also ranks the requests by KV length (longest first; ties by index) into
-// p.order, which the attention kernel uses to hand out work longest-first.
+// Workgroup 0 also ranks the requests by KV length (longest first; ties by index) and
+// writes one record per rank into p.req: the attention kernel hands out work in that
+// order and takes each request's offsets and status from its record.
 //
 // Tile t of request b covers keys [32t, 32t+32) of that request's stream (prefix, then
 // tail); keys past the end repeat the last key (their probabilities are zero, their
@@ -28,29 +29,91 @@ namespace {
 constexpr int NTHR = 256;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
-// order[rank] = request, ranks by descending (prefix_len + q_len), ties by index
-// (malformed requests count as empty).  O(B^2 / 256) work, bounded by ORDER_MAX_BATCH.
-__device__ void rank_requests(const VerifyParams& p) {
+// req[rank]: ranks by descending (prefix_len + q_len), ties by index (malformed requests
+// count as empty), each with the request's packed offsets (exclusive prefix sums over the
+// requests before it in index order) and the status bits the attention kernel reports
+// for it.  O(B^2 / 256) work for the ranks, bounded by ORDER_MAX_BATCH; larger batches
+// keep the index order.
+__device__ void index_requests(const VerifyParams& p) {
   __shared__ int s_cost[ORDER_MAX_BATCH];
+  __shared__ int64_t s_q[NTHR], s_kv[NTHR], s_t[NTHR];
+  __shared__ int s_f[NTHR];
   const int B = p.batch;
-  if (B > ORDER_MAX_BATCH) {
-    for (int b = threadIdx.x; b < B; b += NTHR) p.order[b] = b;
-    return;
-  }
-  for (int b = threadIdx.x; b < B; b += NTHR) {
-    const int t = p.q_len[b], pl = p.prefix_len[b];
-    const bool bad = t < 1 || t > p.max_q_len || pl < 0 || pl > MAX_REQUEST_KEYS - t;
-    s_cost[b] = bad ? 0 : pl + t;
+  const int tid = threadIdx.x;
+  const bool ranked = B <= ORDER_MAX_BATCH;
+  if (ranked) {
+    for (int b = tid; b < B; b += NTHR) {
+      const int t = p.q_len[b], pl = p.prefix_len[b];
+      const bool bad = t < 1 || t > p.max_q_len || pl < 0 || pl > MAX_REQUEST_KEYS - t;
+      s_cost[b] = bad ? 0 : pl + t;
+    }
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < B; b += NTHR) {
-    const int cb = s_cost[b];
-    int rank = 0;
-    for (int i = 0; i < B; ++i) {
-      const int ci = s_cost[i];
-      rank += (ci > cb) || (ci == cb && i < b);
+  int64_t q_run = 0, kv_run = 0, t_run = 0;
+  int f_run = 0;
+  for (int b0 = 0; b0 < B; b0 += NTHR) {
+    const int b = b0 + tid;
+    int t = 0, pl = 0, own = 0, later = 0;
+    int64_t kvl = 0, tiles = 0;
+    if (b < B) {
+      t = p.q_len[b];
+      pl = p.prefix_len[b];
+      own = (t < 1 || t > p.max_q_len ? ST_BAD_QLEN : 0) | (pl < 0 ? ST_BAD_PREFIX : 0);
+      // what this request means for every later one: their offsets are unknown, or (key
+      // count over the limit) the pre-pass stops converting tiles here
+      later = own | (!own && pl > MAX_REQUEST_KEYS - t ? ST_OVERFLOW : 0);
+      kvl = (int64_t)pl + t;
+      tiles = (kvl + TILE_KEYS - 1) / TILE_KEYS;
     }
-    p.order[rank] = b;
+    // inclusive scans across the block (Hillis-Steele)
+    s_q[tid] = t;
+    s_kv[tid] = kvl;
+    s_t[tid] = tiles;
+    s_f[tid] = later;
+    __syncthreads();
+    for (int off = 1; off < NTHR; off <<= 1) {
+      const int64_t aq = tid >= off ? s_q[tid - off] : 0;
+      const int64_t akv = tid >= off ? s_kv[tid - off] : 0;
+      const int64_t at = tid >= off ? s_t[tid - off] : 0;
+      const int af = tid >= off ? s_f[tid - off] : 0;
+      __syncthreads();
+      s_q[tid] += aq;
+      s_kv[tid] += akv;
+      s_t[tid] += at;
+      s_f[tid] |= af;
+      __syncthreads();
+    }
+    if (b < B) {
+      ReqRec r;
+      r.b = b;
+      r.q_len = t;
+      r.prefix_len = pl;
+      r.qoff = q_run + s_q[tid] - t;
+      r.kvoff = kv_run + s_kv[tid] - kvl;
+      r.tbase = t_run + s_t[tid] - tiles;
+      int flag = f_run | (tid > 0 ? s_f[tid - 1] : 0) | own;
+      if (!flag && (r.qoff + t > p.total_q || r.kvoff + kvl > p.total_kv ||
+                    pl > MAX_REQUEST_KEYS - t))
+        flag |= ST_OVERFLOW;
+      if (!flag && r.tbase + tiles > p.k16_tiles) flag |= ST_OVERFLOW;
+      r.flag = flag;
+      r.pad[0] = r.pad[1] = r.pad[2] = 0;
+      int rank = b;
+      if (ranked) {
+        const int cb = s_cost[b];
+        rank = 0;
+        for (int i = 0; i < B; ++i) {
+          const int ci = s_cost[i];
+          rank += (ci > cb) || (ci == cb && i < b);
+        }
+      }
+      p.req[rank] = r;
+    }
+    q_run += s_q[NTHR - 1];
+    kv_run += s_kv[NTHR - 1];
+    t_run += s_t[NTHR - 1];
+    f_run |= s_f[NTHR - 1];
+    __syncthreads();
   }
 }
 
@@ -100,7 +163,7 @@ __global__ __launch_bounds__(NTHR) void prepass_kernel(VerifyParams p) {
     t_run += s_scan_t[NTHR - 1];
     __syncthreads();
   }
-  if (g == 0) rank_requests(p);
+  if (g == 0) index_requests(p);
   // Malformed inputs: the attention kernel flags a malformed request and skips it and
   // every request after it (their packed offsets are unknown), but runs the requests
   // before it; so tiles are converted exactly for the requests before the first
