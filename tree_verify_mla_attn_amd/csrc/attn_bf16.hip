@@ -104,9 +104,10 @@ template <int S> __device__ __forceinline__ u32x4* krope() {
 // global_load_lds, is counted by the compiler's wait insertion as a vector-memory
 // operation only, so LDS reads issued while copies are in flight keep exact lgkmcnt
 // waits instead of draining every outstanding LDS read.
-__device__ __forceinline__ void dma16(const char* uniform_base, unsigned lane_off, u32x4* lds_base) {
+__device__ __forceinline__ void dma16(const char* uniform_base, unsigned lane_off, u32x4* lds_base,
+                                      bool live = true) {
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_base, (short)0, -1, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_base, (short)0, live ? -1 : 0, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)lds_base, 16, (int)lane_off, 0, 0,
                                            0);
 }
@@ -114,9 +115,12 @@ __device__ __forceinline__ void dma16(const char* uniform_base, unsigned lane_of
 // One fp16 latent row (1 KB, already in its LDS image) per DMA: row 8w + n of the tile
 // behind `rsrc` (one descriptor per tile), selected by the scalar offset (8w + n) KB.
 // (The immediate offset of an LDS-destination load moves the LDS address too, so it
-// stays 0.)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* uniform_tile) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_tile, (short)0, -1, 0x00020000);
+// stays 0.)  A copy that is not `live` gets a zero-sized buffer: every lane is out of
+// range, so it reads no memory and completes at once.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* uniform_tile,
+                                                            bool live = true) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_tile, (short)0, live ? -1 : 0,
+                                           0x00020000);
 }
 template <int S, int N>
 __device__ __forceinline__ void dma_k16_row(__amdgpu_buffer_rsrc_t rsrc, int wave, unsigned lane_off) {
@@ -128,13 +132,13 @@ __device__ __forceinline__ void dma_k16_row(__amdgpu_buffer_rsrc_t rsrc, int wav
 // wave: lane l moves chunk 2w + (l >> 5) of key l & 31 into slot 64w + l.
 template <int S>
 __device__ __forceinline__ void dma_rope(const char* k_rope_req, int key0, int key_last, int wave,
-                                         int lane) {
+                                         int lane, bool live = true) {
   // recomputed from an opaque lane id on every call: kept live across the KV loop, the
   // key index would be spilled, and its reload's vmcnt(0) would wait for this tile's copies
   asm volatile("" : "+v"(lane));
   const int k = min(key0 + (lane & 31), key_last);
   dma16(k_rope_req, (unsigned)k * (DR * 2) + (unsigned)(2 * wave + (lane >> 5)) * 16u,
-        krope<S>() + wave * 64);
+        krope<S>() + wave * 64, live);
 }
 
 // Issue the DMA of tile `tile` (keys [key0, key0+32)) into stage S.  Wave w moves fp16
@@ -467,6 +471,7 @@ struct TripStream {
   const __amdgpu_buffer_rsrc_t rsrc;
   const char* k_rope_req;
   const int key0s, lasts, wave, lane, dl, j, par;
+  const bool live;  // the copy is of a tile the loop still needs
   SoftmaxSteps& sm;
   int resc;
   u32x4 ka[KA + 1];
@@ -476,12 +481,12 @@ struct TripStream {
   __device__ __forceinline__ TripStream(f32x16& s_, f32x16 (&o_)[16], const u32x4 (&qf_)[36],
                                         int lane_, int wave_, const char* dma_tile,
                                         const char* k_rope_req_, int k_key0, int key_last,
-                                        int j_, SoftmaxSteps& sm_)
+                                        int j_, bool live_, SoftmaxSteps& sm_)
       : s(s_), o(o_), qf(qf_), fr(lane_), vf(k16<SV>(), lane_, wave_ * 256),
-        rsrc(tile_rsrc(dma_tile)), k_rope_req(k_rope_req_),
+        rsrc(tile_rsrc(dma_tile, live_)), k_rope_req(k_rope_req_),
         key0s(__builtin_amdgcn_readfirstlane(k_key0)),
         lasts(__builtin_amdgcn_readfirstlane(key_last)), wave(wave_), lane(lane_),
-        dl(lane_), j(j_), par(j_ & 1), sm(sm_), resc(-1) {}
+        dl(lane_), j(j_), par(j_ & 1), live(live_), sm(sm_), resc(-1) {}
 
   // P fragment (key step ks, row block rb): lane `lane` of the owner wave's softmax.
   __device__ __forceinline__ f16x8 pfrag(int ks, int rb) const {
@@ -546,7 +551,7 @@ struct TripStream {
         if constexpr (N < 8)
           dma_k16_row<SD, N>(rsrc, wave, (unsigned)dl * 16u);
         else
-          dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl);
+          dma_rope<SD>(k_rope_req, key0s, lasts, wave, dl, live);
       }
       // the score chain starts from zero: s held tile j's scores, consumed last trip
       if constexpr (QK >= 0) s = mfma_qk(QK, ka[QK % (KA + 1)], qf[QK], QK == 0 ? f32x16{} : s);
@@ -599,13 +604,15 @@ struct TileLoop {
                                  : 0xffffffffu);
     SoftmaxSteps sm{s_cur, st, c, masked, vis, lane, wave, j + 1};
     // One stream for every trip (a second PV call site would cost the accumulators their
-    // fixed AGPRs).  On the last trip its copy repeats the last tile into the stage tile
-    // j-1 used: a harmless refill of a stage nobody reads any more (waited for before the
-    // epilogue reuses the ring).
+    // fixed AGPRs).  On the last two trips there is no tile j+2: the copy goes through a
+    // zero-sized buffer, so it reads nothing and completes at once (it zero-fills a stage
+    // nobody reads any more), and neither the next barrier nor the epilogue waits on memory.
     const int jd = min(j + 2, n_tiles - 1);
     TripStream<(ST + 1) % 3, (ST + 2) % 3, ST> ts(s_cur, o, qf, lane, wave,
                                                   k16 + (int64_t)jd * TILE_BYTES, k_rope,
-                                                  k_begin + (j + 2) * BN, key_last, j, sm);
+                                                  k_begin + (j + 2) * BN, key_last, j,
+                                                  __builtin_amdgcn_readfirstlane(j + 2 < n_tiles) != 0,
+                                                  sm);
     ts.run();
   }
 };
@@ -901,10 +908,28 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_tot > 0.0f ? st.m * LN2 + logf(l_tot) : -INFINITY;
   if (lane < 32) sInv[wave * 32 + lane] = inv;
-  // The tile ring is free once every wave has finished the last tile and the last trip's
-  // refill has landed.
+  // The tile ring is free once every wave has finished the last tile (the last trips'
+  // copies read nothing and are done at once).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // The row's lse, before the output (no wait after it then holds the output stores
+  // back), addressed from the tile's uniform base and a lane id recomputed here, so that
+  // no per-lane 64-bit address stays live across the KV loop.
+  int el = lane;  // the lane id, recomputed: lane-derived offsets are not kept across the loop
+  asm volatile("" : "+v"(el));
+  {
+    const int rloc = wave * 32 + (el & 31);  // row within the row tile
+    float* const lse_tile = (piece >= 0 ? p.piece_lse + (int64_t)pslot * BM
+                             : S == 1  ? p.out_lse + qoff * H + m0
+                                       : p.part_lse + (int64_t)split * p.total_q * H + qoff * H + m0);
+    if (m0 + rloc < rows && (el >> 5) == 0) {
+      lse_tile[rloc] = lse;
+      // a piece's lse may be -inf (no visible key); NaN still means non-finite data, and
+      // the piece merge leaves such rows unwritten
+      if ((piece < 0 ? !(fabsf(lse) < INFINITY) : __builtin_isnan(lse)) && p.status)
+        atomicOr(p.status, ST_NONFINITE);
+    }
+  }
   const int trows = min(BM, rows - m0);  // rows of this row tile that exist
   // The workgroup's rows are consecutive global rows; this wave writes features
   // [128 w, 128 w + 128) of each.
@@ -917,7 +942,7 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
   // one row block (32 rows x 128 features) at a time, and every store instruction then
   // writes 512 contiguous bytes of two rows.
   LDS_AS char* stage = (LDS_AS char*)(LDS_AS void*)((wave < 2) ? sK16a : sK16b) + (wave & 1) * EPI_WAVE_BYTES;
-  const int r = lane & 31;
+  const int r = el & 31, eh = el >> 5;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     if (rb * 32 >= trows) continue;
@@ -932,36 +957,24 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 v = {t[4 * q4] * ir, t[4 * q4 + 1] * ir, t[4 * q4 + 2] * ir,
                          t[4 * q4 + 3] * ir};
-        *(LDS_AS f32x4*)(stage + r * EPI_ROW_BYTES + (fb * 32 + q4 * 8 + h * 4) * 4) = v;
+        *(LDS_AS f32x4*)(stage + r * EPI_ROW_BYTES + (fb * 32 + q4 * 8 + eh * 4) * 4) = v;
       }
     }
     wave_sync();
     f32x4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      v[i] = *(const LDS_AS f32x4*)(stage + (2 * i + h) * EPI_ROW_BYTES + r * 16);
-    float* dst = out + (int64_t)(rb * 32 + h) * DL + r * 4;
+      v[i] = *(const LDS_AS f32x4*)(stage + (2 * i + eh) * EPI_ROW_BYTES + r * 16);
+    float* dst = out + (int64_t)(rb * 32 + eh) * DL + r * 4;
     if (rb * 32 + 32 <= trows) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (rb * 32 + 2 * i + h < trows) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
+        if (rb * 32 + 2 * i + eh < trows) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
     }
     wave_sync();
-  }
-  if (row_ok && h == 0) {
-    if (piece >= 0)
-      p.piece_lse[(int64_t)pslot * BM + (row - m0)] = lse;
-    else if (S == 1)
-      p.out_lse[grow] = lse;
-    else
-      p.part_lse[(int64_t)split * p.total_q * H + grow] = lse;
-    // a piece's lse may be -inf (no visible key); NaN still means non-finite data, and
-    // the piece merge leaves such rows unwritten
-    if ((piece < 0 ? !(fabsf(lse) < INFINITY) : __builtin_isnan(lse)) && p.status)
-      atomicOr(p.status, ST_NONFINITE);
   }
 }
 
