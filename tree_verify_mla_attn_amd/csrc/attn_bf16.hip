@@ -966,13 +966,16 @@ __global__ __launch_bounds__(NTHR, 1) void verify_attn_bf16_kernel(VerifyParams 
     for (int i = 0; i < 16; ++i)
       v[i] = *(const LDS_AS f32x4*)(stage + (2 * i + eh) * EPI_ROW_BYTES + r * 16);
     float* dst = out + (int64_t)(rb * 32 + eh) * DL + r * 4;
+    // streaming stores: the output is not read again by this kernel
     if (rb * 32 + 32 <= trows) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
+      for (int i = 0; i < 16; ++i)
+        __builtin_nontemporal_store(v[i], (f32x4*)(dst + (int64_t)(2 * i) * DL));
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (rb * 32 + 2 * i + eh < trows) *(f32x4*)(dst + (int64_t)(2 * i) * DL) = v[i];
+        if (rb * 32 + 2 * i + eh < trows)
+          __builtin_nontemporal_store(v[i], (f32x4*)(dst + (int64_t)(2 * i) * DL));
     }
     wave_sync();
   }
