@@ -38,14 +38,21 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 
-# the sources of the kernel whose HBM counters are stored (the bf16 attention kernel)
+# the sources of the kernels whose HBM counters are stored (every kernel of a bf16 call)
 KERNEL_SOURCES = ("tree_verify_mla_attn_amd/csrc/attn_bf16.hip",
-                  "tree_verify_mla_attn_amd/csrc/common.h")
+                  "tree_verify_mla_attn_amd/csrc/common.h",
+                  "tree_verify_mla_attn_amd/csrc/prepass.hip",
+                  "tree_verify_mla_attn_amd/csrc/merge.hip",
+                  "tree_verify_mla_attn_amd/csrc/capi.hip")
+# what the path computes in: bf16 inputs, fp16 MFMA for the latent dims (Q and the latent
+# rows converted exactly), bf16 MFMA for the rope dims, fp32 accumulation and softmax
+DTYPE_LABEL = {"bf16": "bf16 in, fp16/bf16 MFMA, fp32 acc",
+               "fp32": "fp32 in, fp32 MFMA, fp32 acc"}
 
 
 def kernel_source_digest():
-    """sha256 over the bf16 attention kernel's sources: stored HBM counter readings are
-    used only while it still matches the digest recorded with them."""
+    """sha256 over the bf16 call's kernel sources: stored HBM counter readings are used
+    only while it still matches the digest recorded with them."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -54,23 +61,37 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
+PHASE_KERNELS = ("fill_nan_kernel", "verify_attn_bf16_kernel", "verify_attn_f32_kernel",
+                 "piece_merge_kernel", "lse_merge_kernel")
+
+
 def measured_traffic(path, workload, splits):
-    """HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE readings
-    (KiB per dispatch, each scaled by the factor a plain device copy of known size gave),
-    or None when absent, for another workload, or taken on other kernel sources."""
+    """HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE readings (KiB per
+    dispatch of every kernel of the call, each counter scaled by the factor a plain
+    256 MiB device copy gave): the attention phase's kernels (the roofline's kernel) and
+    the whole call (pre-pass included).  None when absent, for another workload, or taken
+    on other kernel sources."""
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            tj = json.load(f)
+            doc = json.load(f)
     except (OSError, ValueError):
         return None
-    if tj.get("workload") != workload or tj.get("num_splits") != splits \
-            or tj.get("kernel_source_sha256") != kernel_source_digest():
-        return None
-    fetch = tj["fetch_kib_per_dispatch"] * tj["fetch_copy_factor"] * 1024
-    write = tj["write_kib_per_dispatch"] * tj["write_copy_factor"] * 1024
-    return {"bytes": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write)}
+    for e in doc.get("entries", []):
+        if e.get("workload") != workload or e.get("num_splits") != splits \
+                or e.get("kernel_source_sha256") != kernel_source_digest():
+            continue
+        ff, wf = e["fetch_copy_factor"] * 1024, e["write_copy_factor"] * 1024
+        per = {k: {"fetch": round(v["fetch_kib"] * ff), "write": round(v["write_kib"] * wf)}
+               for k, v in e["kernels"].items()}
+        phase = [v for k, v in per.items() if k in PHASE_KERNELS]
+        return {"bytes": sum(v["fetch"] + v["write"] for v in phase),
+                "fetch_bytes": sum(v["fetch"] for v in phase),
+                "write_bytes": sum(v["write"] for v in phase),
+                "call_bytes": sum(v["fetch"] + v["write"] for v in per.values()),
+                "per_kernel": per}
+    return None
 
 
 def parse():
@@ -473,7 +494,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": DTYPE_LABEL[dtype],
         "data": "synthetic (seeded N(0,1) MLA tensors, best-first draft trees)",
         "config": {"workload": inp.name, "batch": inp.batch, "heads": inp.num_heads,
                    "q_len": int(inp.max_q_len), "total_q": inp.total_q, "total_kv": inp.total_kv,
@@ -487,7 +508,9 @@ def main():
                 "peak_GBs": HBM_PEAK_GBS,
                 "frac": round(alg_bytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "measured": traffic,
-                "measured_GBs": round(traffic["bytes"] / (ev_ms * 1e-3) / 1e9, 1) if traffic else None},
+                "measured_GBs": round(traffic["bytes"] / (ev_ms * 1e-3) / 1e9, 1) if traffic else None,
+                "call_bytes_over_algorithmic":
+                    round(traffic["call_bytes"] / alg_bytes, 3) if traffic else None},
         "call_ms_percentiles": {"p10": round(pct(call_each, 0.1), 5),
                                 "median": round(pct(call_each, 0.5), 5),
                                 "p90": round(pct(call_each, 0.9), 5),
