@@ -138,7 +138,7 @@ int32_t setup(const void* q_lat, const void* q_rope, const void* kv_lat, const v
     for (int x = 0; x < kdt::NUM_XCD; ++x) {
       const kdt::XcdCut c = kdt::xcd_cut(batch, p.m_tiles, x);
       if (c.whole > kCutMaxRounds * kdt::CUS_PER_XCD) { p.cut = 0; break; }
-      if (c.left) p.cut = 1;
+      p.cut = std::max(p.cut, c.left);
     }
   }
   return KDTREE_OK;

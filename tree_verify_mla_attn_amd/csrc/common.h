@@ -63,7 +63,7 @@ struct VerifyParams {
   int64_t k16_tiles; // capacity of `k16` in tiles
   // Last-round cut (bf16, one split): each XCD's units after its whole rounds of
   // CUS_PER_XCD run as key pieces, written here and merged by launch_piece_merge.
-  int32_t cut;         // 0: off
+  int32_t cut;         // 0: off; else the most units any XCD's queue has cut (1..16)
   int32_t piece_slots; // piece slots of the area below: CUS_PER_XCD per XCD that has work
   float* piece_o;      // [piece_slots pieces, 128 rows, 512]
   float* piece_lse;    // [piece_slots pieces, 128 rows]

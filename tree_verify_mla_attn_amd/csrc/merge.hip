@@ -23,6 +23,8 @@ namespace {
 
 constexpr int MERGE_ROWS = 4;  // rows (wavefronts) per 256-thread workgroup
 constexpr int MERGE_UNROLL = 4;
+constexpr int PIECE_UNROLL = 8;
+static_assert(PIECE_ROWS % MERGE_ROWS == 0, "whole row tiles per piece-merge grid");
 
 __device__ __forceinline__ float wave_max_f(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -103,7 +105,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   if (lane == 0) out_lse[row] = wsum > 0.0f ? big + logf(wsum) : -INFINITY;
 }
 
-// Piece merge of the last-round cut: one wavefront per (XCD, cut unit, row).  Lane k < K
+// Piece merge of the last-round cut: one wavefront per (XCD, cut unit, row), for units
+// 0 .. max_left - 1 of each XCD (max_left: the most units any XCD cut).  Lane k < K
 // holds the lse of piece k; the same weights as above combine the K pieces' outputs into
 // the unit's output row (the pieces cover the request's whole key range).  A row whose
 // piece lse is still NaN in some piece was not computed (a skipped request, or a row past
@@ -115,12 +118,12 @@ __global__ __launch_bounds__(256) void piece_merge_kernel(const float* __restric
                                                           float* __restrict__ out_lse,
                                                           int32_t* __restrict__ status,
                                                           int groups, int m_tiles,
-                                                          int64_t total_rows) {
+                                                          int max_left, int64_t total_rows) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * MERGE_ROWS + (threadIdx.x >> 6);  // (xcd, unit, row)
   const int row = w % PIECE_ROWS;
-  const int unit = (w / PIECE_ROWS) % CUS_PER_XCD;
-  const int xcd = w / (PIECE_ROWS * CUS_PER_XCD);
+  const int unit = (w / PIECE_ROWS) % max_left;
+  const int xcd = w / (PIECE_ROWS * max_left);
   if (xcd >= NUM_XCD) return;
   const XcdCut cut = xcd_cut(groups, m_tiles, xcd);
   if (unit >= cut.left) return;
@@ -137,12 +140,29 @@ __global__ __launch_bounds__(256) void piece_merge_kernel(const float* __restric
   const float wsum = wave_sum_f(wl);
   const float* src = piece_o + (s0 * PIECE_ROWS + row) * DL + lane * 4;
   float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-  for (int k = 0; k < k_n; ++k) {
-    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
-    const float4 v0 = *(const float4*)(src + (int64_t)k * PIECE_ROWS * DL);
-    const float4 v1 = *(const float4*)(src + (int64_t)k * PIECE_ROWS * DL + 256);
-    a0.x += wk * v0.x; a0.y += wk * v0.y; a0.z += wk * v0.z; a0.w += wk * v0.w;
-    a1.x += wk * v1.x; a1.y += wk * v1.y; a1.z += wk * v1.z; a1.w += wk * v1.w;
+  // PIECE_UNROLL pieces' loads in flight at a time (one at a time, the wave would wait a
+  // full memory latency per piece); the sum still runs over the pieces in order
+  for (int k0 = 0; k0 < k_n; k0 += PIECE_UNROLL) {
+    float4 v0[PIECE_UNROLL], v1[PIECE_UNROLL];
+    float ws[PIECE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PIECE_UNROLL; ++u) {
+      const int k = k0 + u;  // uniform
+      ws[u] = 0.0f;
+      v0[u] = v1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < k_n) {
+        ws[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+        v0[u] = *(const float4*)(src + (int64_t)k * PIECE_ROWS * DL);
+        v1[u] = *(const float4*)(src + (int64_t)k * PIECE_ROWS * DL + 256);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PIECE_UNROLL; ++u) {
+      a0.x += ws[u] * v0[u].x; a0.y += ws[u] * v0[u].y;
+      a0.z += ws[u] * v0[u].z; a0.w += ws[u] * v0[u].w;
+      a1.x += ws[u] * v1[u].x; a1.y += ws[u] * v1[u].y;
+      a1.z += ws[u] * v1[u].z; a1.w += ws[u] * v1[u].w;
+    }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   float* dst = out_lat + grow * DL + lane * 4;
@@ -160,11 +180,12 @@ __global__ __launch_bounds__(256) void piece_merge_kernel(const float* __restric
 hipError_t launch_piece_merge(const VerifyParams& p, hipStream_t stream) {
   if (!p.cut) return hipSuccess;
   if (p.piece_slots <= 0 || p.piece_slots > PIECE_SLOTS) return hipErrorInvalidValue;
-  const int blocks = p.piece_slots * PIECE_ROWS / MERGE_ROWS;
+  if (p.cut < 1 || p.cut > CUS_PER_XCD / 2) return hipErrorInvalidValue;  // >= 2 pieces a unit
+  const int xcds = p.piece_slots / CUS_PER_XCD;  // the XCDs that received work
+  const int blocks = xcds * p.cut * (PIECE_ROWS / MERGE_ROWS);
   hipLaunchKernelGGL(piece_merge_kernel, dim3(blocks), dim3(256), 0, stream, p.piece_o,
                      p.piece_lse, p.piece_desc, p.out_lat, p.out_lse, p.status, p.batch,
-                     p.m_tiles,
-                     p.total_q * p.num_heads);
+                     p.m_tiles, (int)p.cut, p.total_q * p.num_heads);
   return hipGetLastError();
 }
 
