@@ -185,6 +185,12 @@ __device__ __forceinline__ float log2_seq(float x) {
 // as u rises, up to the few-ulp rounding of the two logarithms.
 __device__ __forceinline__ float gumbel_log2(float u) { return log2_seq(-log2_seq(u)); }
 
+// The same with the hardware base-2 logarithm (v_log_f32, within about an ulp), for the
+// pruning bound only: it never enters a key.
+__device__ __forceinline__ float gumbel_log2_hw(float u) {
+  return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+}
+
 // u <= 1 - 2^-24 gives -log2(-log2 u) <= 23.47, so no key exceeds its scaled logit by more
 // than this (plus a relative margin for the rounding of large scaled logits).
 constexpr float KEY_HEADROOM = 24.0f;
@@ -237,7 +243,9 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
         }
       continue;
     }
-    if ((step & 7) == 0) {  // a stale bound is still a bound
+    // A stale bound is still a bound: it is refreshed every step at first, while it is
+    // far below the winner (the first step prunes nothing), then every eighth step.
+    if (step < 8 || (step & 7) == 0) {
       wave_best = fmaxf(wave_max_f(bz), s_bound);
       if ((tid & 63) == 0 && wave_best > s_bound) s_bound = wave_best;
     }
@@ -253,14 +261,20 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
     unsigned w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) w[k] = (unsigned)(c[k >> 1] >> (32 * (k & 1)));
-    // Second test, with the block's own uniforms: u rises with its word and a key falls
-    // with gumbel_log2(u), so no key of the block exceeds sm - gumbel_log2(u of the
-    // largest word).  The margin covers the logarithms' rounding (a few ulp each, at most
-    // ~6e-7 absolute through the outer one) and the rounding of the products.
+    // Second test, with the block's own uniforms.  u rises with its word and the exact
+    // g(u) = log2(-log2 u) falls with u, so with u_max the uniform of the largest word,
+    // every key of the block is at most sm - g(u_max) plus rounding.  The test evaluates
+    // g(u_max) with the hardware logarithm; the margin covers, with a factor of two to
+    // spare, the error of gumbel_log2 against g (its inner logarithm within 3.6e-7
+    // relative, which moves the outer one by at most 5.2e-7, plus 3 ulp of the result),
+    // the error of gumbel_log2_hw against g (2 ulp each way assumed: 3.5e-7 plus 2 ulp),
+    // and the rounding of the key's subtraction and of this expression: in all, less than
+    // 8.7e-7 + 2^-20 |gmin| + 2^-22 |sm|.  A skipped block thus holds only keys strictly
+    // below the bound, and the draw is the same as without the test.
     const unsigned wmax = max(max(max(w[0], w[1]), max(w[2], w[3])),
                               max(max(w[4], w[5]), max(w[6], w[7])));
-    const float gmin = gumbel_log2(uniform_of(wmax));
-    if (!(sm - gmin + (fabsf(sm) + fabsf(gmin)) * 0x1p-20f + 0x1p-20f >= best)) continue;
+    const float gmin = gumbel_log2_hw(uniform_of(wmax));
+    if (!(sm - gmin + (fabsf(sm) + fabsf(gmin)) * 0x1p-19f + 0x1p-19f >= best)) continue;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float z = mul_sub_rounded(x[k], cs, gumbel_log2(uniform_of(w[k])));
