@@ -3,6 +3,7 @@
     python -m tree_verify_mla_attn_amd.profile_summary trace  KT_DIR BENCH_LOG WARMUP STEPS CMD
     python -m tree_verify_mla_attn_amd.profile_summary traffic FETCH_CSV WRITE_CSV WORKLOAD SPLITS CALLS CMD1 CMD2
     python -m tree_verify_mla_attn_amd.profile_summary counters CSV CMD
+    python -m tree_verify_mla_attn_amd.profile_summary bench-table DIR [DIR ...]
 
 `trace` reads a --kernel-trace --stats run of bench.py (its kernel trace CSV and the JSON
 line the same run printed) and recomputes the roofline fraction from the traced kernel
@@ -10,6 +11,8 @@ durations of the timed steps.  `traffic` reads one FETCH_SIZE and one WRITE_SIZE
 run of bench.py --calibrate-copy, scales each counter by what it reads for the 256 MiB
 calibration copy, and merges the per-kernel bytes into profiles/traffic.json, where
 bench.py finds them.  `counters` prints per-kernel means of any other counter run.
+`bench-table` tabulates the JSON lines of `bench.py --workload W` runs (W = 1..5, logged
+as DIR/bench_wW.log), one table per DIR (one box each).
 """
 from __future__ import annotations
 
@@ -186,6 +189,45 @@ def counters(csv_path: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def bench_table(dirs) -> str:
+    out = ["# bench.py lines of the five workloads (defaults), one MI355X per table",
+           "",
+           "Command, from the repository root, one run per workload, back to back on one box:",
+           "  python3 bench.py --workload W          (W = 1..5; W = 4 is the default)",
+           "",
+           "value = algorithmic TFLOP/s of the whole call (pre-pass + attention + merge) from the",
+           "wall clock around the timed steps; frac = the attention phase (the roofline kernel",
+           "column) from HIP events on its stream, over the dtype's dense MFMA peak (bf16 path:",
+           "2500 TFLOP/s; fp32 path: 157.3); HBM frac = algorithmic bytes over the phase time",
+           "against 8 TB/s; call bytes = the calibrated FETCH_SIZE + WRITE_SIZE bytes of every",
+           "kernel of the call (profiles/traffic.json, stored for the bf16 workloads) over the",
+           "algorithmic bytes; GEMM = torch's 8192^3 bf16 GEMM on the same box, as a gauge of",
+           "the box; cpu = the float64 oracle's TFLOP/s on a bounded sample."]
+    for i, d in enumerate(dirs):
+        lines = []
+        for w in range(1, 6):
+            path = os.path.join(d, f"bench_w{w}.log")
+            if os.path.exists(path):
+                lines.append((w, bench_line(path)))
+        out += ["", f"## Box {i + 1} (logs in {d})", "",
+                "| W | workload | splits | dtype | value TFLOP/s | ms/step | steps/s | phase kernel "
+                "| phase TFLOP/s | frac of MFMA peak | HBM frac | call bytes / algorithmic "
+                "| GEMM bf16 TFLOP/s | cpu oracle TFLOP/s |",
+                "|" + "---|" * 14]
+        for w, ln in lines:
+            r, h, c = ln["roofline"], ln["hbm"], ln["config"]
+            cb = h.get("call_bytes_over_algorithmic")
+            out.append(f"| {w} | {c['workload']} | {c['num_splits']} | {ln['dtype']} | "
+                       f"{ln['value']} | {ln['ms_per_step']} | {ln['steps_per_s']} | "
+                       f"{r['kernel']} | {r['achieved']} | {r['frac']} | {h['frac']} | "
+                       f"{'-' if cb is None else cb} | "
+                       f"{ln.get('measured_peaks', {}).get('gemm_bf16_TFLOPs', '-')} | "
+                       f"{ln['cpu_baseline']['value']} |")
+        out += ["", "Full lines:", ""]
+        out += ["    " + json.dumps(ln) for _, ln in lines]
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv[0] == "trace":
         sys.stdout.write(trace(argv[1], argv[2], int(argv[3]), int(argv[4]), argv[5]))
@@ -194,6 +236,8 @@ def main(argv):
                          indent=1))
     elif argv[0] == "counters":
         sys.stdout.write(counters(argv[1], argv[2]))
+    elif argv[0] == "bench-table":
+        sys.stdout.write(bench_table(argv[1:]))
     else:
         raise SystemExit(__doc__)
 
