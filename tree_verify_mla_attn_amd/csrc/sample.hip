@@ -191,6 +191,24 @@ __device__ __forceinline__ float gumbel_log2_hw(float u) {
   return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
 }
 
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
+// Whether a key RN(RN(x cs) - gumbel_log2(u)) can reach `best`, given sx >= RN(x cs) and
+// gh = gumbel_log2_hw(u') with u' >= u (u' = u for one entry, the block's largest
+// uniform for a block; the exact log2(-log2 u) falls as u rises).  False only when every
+// such key is strictly below `best`.  The margin covers, with a factor of two to spare,
+// the error of gumbel_log2 against the exact value (its inner logarithm within 3.6e-7
+// relative, which moves the outer one by at most 5.2e-7, plus 3 ulp of the result; the
+// bound is pinned over every uniform the draw can produce), the error of gumbel_log2_hw
+// (2 ulp each way assumed: 3.5e-7 plus 2 ulp), and the rounding of the key's subtraction
+// and of this expression: in all, less than 8.7e-7 + 2^-20 |gh| + 2^-22 |sx|.
+__device__ __forceinline__ bool could_reach(float sx, float gh, float best) {
+  return sx - gh + (fabsf(sx) + fabsf(gh)) * 0x1p-19f + 0x1p-19f >= best;
+}
+
 // u <= 1 - 2^-24 gives -log2(-log2 u) <= 23.47, so no key exceeds its scaled logit by more
 // than this (plus a relative margin for the rounding of large scaled logits).
 constexpr float KEY_HEADROOM = 24.0f;
@@ -261,22 +279,25 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_tokens_kernel(SamplePar
     unsigned w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) w[k] = (unsigned)(c[k >> 1] >> (32 * (k & 1)));
-    // Second test, with the block's own uniforms.  u rises with its word and the exact
-    // g(u) = log2(-log2 u) falls with u, so with u_max the uniform of the largest word,
-    // every key of the block is at most sm - g(u_max) plus rounding.  The test evaluates
-    // g(u_max) with the hardware logarithm; the margin covers, with a factor of two to
-    // spare, the error of gumbel_log2 against g (its inner logarithm within 3.6e-7
-    // relative, which moves the outer one by at most 5.2e-7, plus 3 ulp of the result),
-    // the error of gumbel_log2_hw against g (2 ulp each way assumed: 3.5e-7 plus 2 ulp),
-    // and the rounding of the key's subtraction and of this expression: in all, less than
-    // 8.7e-7 + 2^-20 |gmin| + 2^-22 |sm|.  A skipped block thus holds only keys strictly
-    // below the bound, and the draw is the same as without the test.
+    // Second test, with the block's own uniforms: u rises with its word, so with u_max
+    // the uniform of the largest word every key of the block is at most sm - g(u_max)
+    // plus rounding (could_reach).  A skipped block holds only keys strictly below the
+    // bound, and the draw is the same as without the test.
     const unsigned wmax = max(max(max(w[0], w[1]), max(w[2], w[3])),
                               max(max(w[4], w[5]), max(w[6], w[7])));
     const float gmin = gumbel_log2_hw(uniform_of(wmax));
-    if (!(sm - gmin + (fabsf(sm) + fabsf(gmin)) * 0x1p-19f + 0x1p-19f >= best)) continue;
+    if (!could_reach(sm, gmin, best)) continue;
+    // The same test per entry, with its own uniform (no monotonicity step needed): only
+    // entries that could reach the bound get the exact key, whose two fixed-sequence
+    // logarithms cost about ten times the hardware ones.
+    unsigned need = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      need |= could_reach(mul_rounded(x[k], cs), gumbel_log2_hw(uniform_of(w[k])), best) ? 1u << k
+                                                                                     : 0u;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      if (!(need & (1u << k))) continue;
       const float z = mul_sub_rounded(x[k], cs, gumbel_log2(uniform_of(w[k])));
       if (z > bz) {
         bz = z;
