@@ -2,17 +2,22 @@
 
     python -m tree_verify_mla_attn_amd.profile_summary trace  KT_DIR BENCH_LOG WARMUP STEPS CMD
     python -m tree_verify_mla_attn_amd.profile_summary traffic FETCH_CSV WRITE_CSV WORKLOAD SPLITS CALLS CMD1 CMD2
+    python -m tree_verify_mla_attn_amd.profile_summary traffic-text WORKLOAD SPLITS BENCH_LOG
     python -m tree_verify_mla_attn_amd.profile_summary counters CSV CMD
     python -m tree_verify_mla_attn_amd.profile_summary bench-table DIR [DIR ...]
+    python -m tree_verify_mla_attn_amd.profile_summary greedy-trace KT_DIR BENCH_LOG CMD
 
 `trace` reads a --kernel-trace --stats run of bench.py (its kernel trace CSV and the JSON
 line the same run printed) and recomputes the roofline fraction from the traced kernel
 durations of the timed steps.  `traffic` reads one FETCH_SIZE and one WRITE_SIZE counter
 run of bench.py --calibrate-copy, scales each counter by what it reads for the 256 MiB
 calibration copy, and merges the per-kernel bytes into profiles/traffic.json, where
-bench.py finds them.  `counters` prints per-kernel means of any other counter run.
+bench.py finds them; `traffic-text` prints one stored entry beside the algorithmic bytes
+of the workload's bench line.  `counters` prints per-kernel means of any other counter run.
 `bench-table` tabulates the JSON lines of `bench.py --workload W` runs (W = 1..5, logged
-as DIR/bench_wW.log), one table per DIR (one box each).
+as DIR/bench_wW.log), one table per DIR (one box each).  `greedy-trace` reads a kernel
+trace of a default bench.py run (greedy step included) and summarises the builder, pack,
+accept and draw kernels.
 """
 from __future__ import annotations
 
@@ -228,16 +233,76 @@ def bench_table(dirs) -> str:
     return "\n".join(out) + "\n"
 
 
+GREEDY_KERNELS = ("build_ddtree_kernel", "pack_tree_kernel", "tree_accept_kernel")
+
+
+def greedy_trace(kt_dir: str, bench_log: str, cmd: str) -> str:
+    rows = sorted(csv.DictReader(open(os.path.join(kt_dir, "kt_kernel_trace.csv"))),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    per = defaultdict(list)
+    info = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        key = next((k for k in GREEDY_KERNELS if k in name), None)
+        if key is None and "sample_tokens_kernel" in name:
+            key = "sample_tokens_kernel " + ("bf16" if "<true" in name else "fp32")
+        if key is None:
+            continue
+        per[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        info[key] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"],
+                     r["Grid_Size_X"], r["Workgroup_Size_X"])
+    # bench.py draws flat logits first (1 + 10 launches per dtype), then peaked ones
+    for dt in ("fp32", "bf16"):
+        k = "sample_tokens_kernel " + dt
+        if k in per:
+            v = per.pop(k)
+            half = len(v) // 2
+            per[k + " flat"], per[k + " peaked"] = v[:half], v[half:]
+            info[k + " flat"] = info[k + " peaked"] = info.pop(k)
+    g = bench_line(bench_log).get("greedy_step", {})
+    out = ["# rocprofv3 kernel trace: draft-tree build, tree packing, greedy accept, temperature "
+           f"draw ({g.get('batch')} trees, budget {g.get('budget')}, depth {g.get('depth')}, "
+           f"workload {g.get('workload')})",
+           "",
+           "Command (from the repository root, on one MI355X; rocprofv3 run from /tmp with "
+           "TMPDIR=/tmp):",
+           f"  {cmd}",
+           "",
+           "bench.py captures 64 launches of each of the first three kernels in one HIP graph and",
+           "replays it; the temperature draw (node rows x 163840 tokens, T = 0.8) runs 1 + 10",
+           "times each on flat N(0, 2) logits and on peaked ones (12 candidates near +24), fp32",
+           "and bf16.",
+           "",
+           "  kernel | dispatches | avg us | median us | min us | VGPR | AGPR | SGPR | LDS bytes "
+           "| grid | block"]
+    for k in sorted(per):
+        v = sorted(per[k])
+        out.append(f"  {k} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | "
+                   f"{v[0]:.2f} | " + " | ".join(info[k]))
+    out += ["",
+            "The same process's bench.py greedy_step line (graph replay or ten launches between "
+            "two events, per launch):",
+            "  " + json.dumps(g)]
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv[0] == "trace":
         sys.stdout.write(trace(argv[1], argv[2], int(argv[3]), int(argv[4]), argv[5]))
     elif argv[0] == "traffic":
         print(json.dumps(traffic(argv[1], argv[2], argv[3], int(argv[4]), int(argv[5]), argv[6:]),
                          indent=1))
+    elif argv[0] == "traffic-text":
+        entries = json.load(open(TRAFFIC_JSON))["entries"]
+        entry = next(e for e in entries
+                     if e["workload"] == argv[1] and e["num_splits"] == int(argv[2]))
+        sys.stdout.write(traffic_text(entry, bench_line(argv[3])))
     elif argv[0] == "counters":
         sys.stdout.write(counters(argv[1], argv[2]))
     elif argv[0] == "bench-table":
         sys.stdout.write(bench_table(argv[1:]))
+    elif argv[0] == "greedy-trace":
+        sys.stdout.write(greedy_trace(argv[1], argv[2], argv[3]))
     else:
         raise SystemExit(__doc__)
 
