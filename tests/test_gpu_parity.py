@@ -75,6 +75,30 @@ def _mk(seed, parents, prefix, heads, dtype, scale=None):
                              dtype=dtype, scale=scale)
 
 
+def _ramp(seed, dtype, slope):
+    """Scores that move steadily along each request's key stream: every latent key row is
+    c_j + 0.25 N(0, 1) with c_j running linearly from -8 slope to 8 slope over the request's
+    keys, and every query row 0.5 + 0.25 N(0, 1), so that q . k_j ~ 256 c_j.  At the
+    default scale the running maximum then moves by about 14 log2 units per 32-key tile
+    (slope 1: above the rescale threshold on every tile) or the first tile dominates and
+    the later probabilities underflow (slope -1)."""
+    rng = np.random.default_rng(seed)
+    parents = [synth.random_tree(np.random.default_rng(seed + 1), 33), synth.chain_tree(9)]
+    inp = synth.make_inputs(rng, num_heads=16, prefix_lens=[1000, 300], parents=parents,
+                            dtype=dtype)
+    fix = synth.round_to_bf16 if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    kv_off, q_off = inp.kv_offsets(), inp.q_offsets()
+    for b in range(inp.batch):
+        n = int(inp.prefix_len[b] + inp.q_len[b])
+        c = np.linspace(-8.0 * slope, 8.0 * slope, n, dtype=np.float32)[:, None]
+        rows = slice(int(kv_off[b]), int(kv_off[b]) + n)
+        inp.kv_lat[rows] = fix(c + 0.25 * rng.standard_normal((n, 512), dtype=np.float32))
+        qs = slice(int(q_off[b]), int(q_off[b]) + int(inp.q_len[b]))
+        inp.q_lat[qs] = fix(0.5 + 0.25 * rng.standard_normal(inp.q_lat[qs].shape,
+                                                             dtype=np.float32))
+    return inp
+
+
 EDGE = {
     "chain9_p37_h64": lambda dt: _mk(1, [synth.chain_tree(9)], [37], 64, dt),
     "star17_p0_h16": lambda dt: _mk(2, [synth.star_tree(17)], [0], 16, dt),
@@ -94,11 +118,28 @@ EDGE = {
                                      64, dt, scale=-0.08),
 }
 
+# Softmax stress: scores of magnitude 50-160, where the running maximum moves on every
+# tile (rising), or the first tile dominates and later probabilities underflow (falling).
+# bf16 only: the fp32 bound is absolute (1e-5), below what float32 rounding of such
+# scores allows; the bf16 bound scales with the values.
+STRESS = {
+    "large_scale": lambda: _mk(10, [synth.random_tree(np.random.default_rng(32), 33)], [700], 64,
+                               "bf16", scale=1.0),
+    "rising_scores": lambda: _ramp(11, "bf16", 1.0),
+    "falling_scores": lambda: _ramp(13, "bf16", -1.0),
+}
+
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("case", list(EDGE))
 def test_edge_cases(dev, case, dtype):
     full_check(f"{case}/{dtype}", EDGE[case](dtype), dev)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("case", list(STRESS))
+def test_softmax_stress(dev, case, splits):
+    full_check(f"{case}/bf16", STRESS[case](), dev, num_splits=splits)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
