@@ -79,19 +79,33 @@ __device__ __forceinline__ void issue_tile(const float* kv_lat_req, const float*
         (unsigned)(min(row, last) * DR * 4 + ((slot ^ row) & 15) * 16), 0u);
 }
 
+// K fragment kb of this lane (16 bytes: key lane & 15, floats 16 kb + 4 g .. + 3).
 template <int STAGE>
-__device__ __forceinline__ f32x4 qk_tile(const float4 (&qf)[36], int lane) {
+__device__ __forceinline__ float4 k_frag(int kb, int key, int g) {
   const float* kt = ktile<STAGE>();
   const float* kr = kt + STAGE_LAT;
+  return kb < 32 ? *(const float4*)(kt + key * LSTRIDE + 16 * kb + 4 * g)
+                 : *(const float4*)(kr + key * DR + (((kb - 32) * 4 + g) ^ key) * 4);
+}
+
+template <int STAGE>
+__device__ __forceinline__ f32x4 qk_tile(const float4 (&qf)[36], int lane) {
   const int key = lane & 15, g = lane >> 4;
   // Four independent accumulation chains (one per float of the 16-byte operand), summed
   // pairwise at the end: each chain adds 144 products, which keeps the fp32 rounding of
   // the 576-term score well inside the 1e-5 output bound.
   f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};
+  // K fragments are read two k-steps ahead: the MFMAs are asm statements, which the
+  // compiler does not move loads across, so a fragment read just before its MFMAs would
+  // wait out the whole LDS latency at every k-step.
+  constexpr int KA = 2;
+  float4 ka[KA + 1];
+#pragma unroll
+  for (int i = 0; i < KA; ++i) ka[i] = k_frag<STAGE>(i, key, g);
 #pragma unroll
   for (int kb = 0; kb < 36; ++kb) {
-    const float4 a = kb < 32 ? *(const float4*)(kt + key * LSTRIDE + 16 * kb + 4 * g)
-                             : *(const float4*)(kr + key * DR + (((kb - 32) * 4 + g) ^ key) * 4);
+    if (kb + KA < 36) ka[(kb + KA) % (KA + 1)] = k_frag<STAGE>(kb + KA, key, g);
+    const float4 a = ka[kb % (KA + 1)];
     // Q is an AGPR operand of these MFMAs, so the register allocator keeps all 144 Q
     // values in the AGPR file for the whole loop.  Q and O together (272 values) exceed
     // the 256 VGPRs; with Q in VGPRs, O moved between the two files every tile.
