@@ -136,6 +136,12 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[32], const f32x4& pr, int lan
   }
 }
 
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(uint64_t)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 struct RowState32 {
   float m, l;
 };
@@ -221,8 +227,10 @@ void verify_attn_f32_kernel(VerifyParams p) {
     if (bad) atomicOr(&sFlag32, bad);
   }
   __syncthreads();
-  qoff = sRed32[0] + sRed32[1] + sRed32[2] + sRed32[3];
-  kvoff = sRed32[4] + sRed32[5] + sRed32[6] + sRed32[7];
+  // The same in every lane; said so explicitly, or the copies' buffer descriptors built
+  // from them would be treated as per-lane and each copy run in a waterfall loop.
+  qoff = uniform64(sRed32[0] + sRed32[1] + sRed32[2] + sRed32[3]);
+  kvoff = uniform64(sRed32[4] + sRed32[5] + sRed32[6] + sRed32[7]);
   const int T = p.q_len[b];
   const int P = p.prefix_len[b];
   int flag = sFlag32;
